@@ -1,0 +1,79 @@
+"""The seeded workloads have the structure the configs describe, and are reproducible."""
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_205_amd import synth
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "full", "fragmented", "skewed", "large"])
+def test_layout_invariants(name):
+    lay = synth.get(name)
+    lay.check_invariants()
+    L = lay.seq_lens
+    assert L.dtype == np.int32 and lay.block_tables.dtype == np.int32
+    # entries past ceil(L/16) are unassigned, except tiny whose table is a full permutation
+    if name != "tiny":
+        for l in range(lay.n_layers):
+            for b in range(lay.B):
+                assert (lay.block_tables[l, b, synth.nblocks(L[b]):] == -1).all()
+
+
+def test_config_shapes():
+    t = synth.tiny()
+    assert (t.B, t.n_layers, t.num_pages, int(t.seq_lens[0])) == (1, 1, 8, 38)
+    assert sorted(t.block_tables[0, 0].tolist()) == list(range(8))
+    s = synth.small()
+    assert s.num_pages * 32 * 1024 == 128 * 2 ** 20 and s.B == 8 and s.n_layers == 16
+    assert s.seq_lens.min() >= 1 and s.seq_lens.max() <= 512
+    f = synth.full()
+    assert f.kv_bytes_per_step == 4 * 2 ** 30 and f.num_pages == 131072
+    assert f.block_tables[3, 5, 7] == (5 * 16 + 3) * 128 + 7
+    fr = synth.fragmented()
+    assert fr.seq_lens[:4].tolist() == [16, 17, 1025, 2048]
+    assert fr.seq_lens.min() >= 16 and fr.seq_lens.max() <= 2048
+    assert (fr.seq_lens % 16 == 0).any() and (fr.seq_lens % 16 == 1).any()
+    used = sum(synth.nblocks(x) for x in fr.seq_lens) * 16
+    assert fr.num_pages == 2 * used
+    sk = synth.skewed()
+    assert (sk.seq_lens == 2048).sum() == 1 and np.sort(sk.seq_lens)[-2] <= 64
+    assert sk.sigma_k == 3.0
+    lg = synth.large()
+    assert lg.B == 1024 and lg.seq_lens.max() <= 2048 and lg.sigma_k == 3.0
+    per = lg.num_pages // 16
+    for l in (0, 7, 15):
+        row = lg.block_tables[l]
+        used = row[row >= 0]
+        assert used.min() == l * per and used.max() == (l + 1) * per - 1
+
+
+def test_reproducible_and_poisoned():
+    lay = synth.small()
+    k1, v1 = synth.make_pools(lay, "cpu", layers=[0, 5])
+    k2, v2 = synth.make_pools(lay, "cpu", layers=[0, 5])
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    kb = synth.bits(k1)
+    filled = np.zeros((lay.num_pages, 16), bool)
+    for l in (0, 5):
+        p, s = lay.filled_slots(l)
+        filled[p, s] = True
+    assert (kb[~filled] == synth.BF16_NAN_BITS).all()
+    vals = kb[filled].astype(np.uint32)
+    assert not ((vals & 0x7F80) == 0x7F80).any(), "filled slots must be finite"
+    # per-layer streams: layer 5 alone regenerates the same bits
+    k3, _ = synth.make_pools(lay, "cpu", layers=[5])
+    p, s = lay.filled_slots(5)
+    assert np.array_equal(synth.bits(k3)[p, s], kb[p, s])
+    q1 = synth.step_inputs(lay, 3)["q"]
+    q2 = synth.step_inputs(lay, 3)["q"]
+    assert torch.equal(q1, q2) and q1.shape == (8, 32, 64)
+    x = synth.step_inputs(lay, 0)["q"].float()
+    assert abs(x.mean().item()) < 0.05 and abs(x.std().item() - 1) < 0.05
+
+
+def test_sigma_k_three():
+    lay = synth.skewed(B=64, n_layers=1)
+    k, _ = synth.make_pools(lay, "cpu")
+    p, s = lay.filled_slots(0)
+    x = k[torch.from_numpy(p), torch.from_numpy(s)].float()
+    assert abs(x.std().item() - 3.0) < 0.1
