@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is, for each of the 16 layers, ``pa_append`` (this step's token of every
+sequence into its page slot) then ``pa_decode`` (batched paged decode attention
+over the shared BF16 page pool), all on one stream, with every input already
+resident in HBM.  The default workload is the full-context batch: 64 sequences
+at 2048 tokens, 16 layers, 32 query / 8 KV heads, head dim 64, 16-token pages
+(4 GiB of K and V read per step).
+
+Prints one JSON line: effective KV GB/s for the whole step (KV bytes the
+attention must read / step time), µs per step, the roofline of the decode kernel
+(algorithmic bytes per launch / mean launch time from HIP events) and the FP64
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "paged decode attn: effective KV GB/s (% HBM peak), µs/step at batch 64×2048"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the FP64 oracle as it stands, on a bounded sample (runs before
+# the GPU is touched so that worker processes fork from a GPU-free parent).
+
+_CPU = {}
+
+
+def _oracle_seq(item):
+    """append_ref + decode_ref for one (layer, sequence) of the sample; returns its length."""
+    from oracle import append_ref, decode_ref
+    l, b = item
+    d = _CPU[l]
+    kp, vp, bt = d["pages"][b]
+    L = d["L"][b:b + 1]
+    k2, v2 = append_ref(kp, vp, d["k_new"][b:b + 1], d["v_new"][b:b + 1], bt, L)
+    decode_ref(d["q"][b:b + 1], k2, v2, bt, L, d["scale"])
+    return int(L[0])
+
+
+def cpu_baseline(lay, n_layers: int, workers: int):
+    """Time the FP64 oracle (append + decode) on the first n_layers layers of the workload."""
+    import torch
+    from paged_kv_cache_205_amd import synth
+    torch.set_num_threads(1)
+    layers = list(range(min(n_layers, lay.n_layers)))
+    for l in layers:
+        k, v, bt = synth.layer_pages(lay, l, "cpu")
+        k, v = synth.bits(k), synth.bits(v)
+        x = synth.step_inputs(lay, l, "cpu")
+        pages = {}
+        for b in range(lay.B):  # each sequence's own pages, block table renumbered 0..n-1
+            n = synth.nblocks(lay.seq_lens[b])
+            ids = bt[b, :n]
+            pages[b] = (k[ids], v[ids], np.arange(max(n, 1), dtype=np.int32)[None])
+        _CPU[l] = dict(pages=pages, L=lay.seq_lens, q=synth.bits(x["q"]), k_new=synth.bits(x["k_new"]),
+                       v_new=synth.bits(x["v_new"]), scale=lay.scale)
+        del k, v
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    items = [(l, b) for l in layers for b in range(lay.B)]
+    # one core, on the first few items
+    t0 = time.perf_counter()
+    n1 = sum(_oracle_seq(it) for it in items[:max(1, min(8, len(items)))])
+    t1 = time.perf_counter() - t0
+    # all workers (forked before the GPU is touched)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        ntok = sum(pool.map(_oracle_seq, items, chunksize=1))
+    tw = time.perf_counter() - t0
+    return {
+        "value": round(ntok * 2048 / tw / 1e9, 6),  # 2048 bytes of K and V per token per layer
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"layers 0..{layers[-1]} of the same workload, all {lay.B} sequences each "
+                  f"({ntok} tokens, {ntok * 2048 / 1e9:.3f} GB of K+V): append_ref + decode_ref "
+                  f"(FP64 NumPy) in {workers} worker processes, {tw:.1f} s wall",
+        "single_core_GBps": round(n1 * 2048 / t1 / 1e9, 6),
+        "seconds": round(tw, 2),
+    }
+
+
+# ----------------------------------------------------------------------------
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="full", help="workload: full, fragmented, skewed, large, small, tiny")
+    ap.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the workload the oracle runs on")
+    ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from paged_kv_cache_205_amd import synth
+    lay = synth.get(args.config)
+
+    cpu = None
+    if not args.no_cpu:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"cpu baseline: oracle on {workers} workers ...")
+        cpu = cpu_baseline(lay, args.cpu_layers, workers)
+        log(f"cpu baseline: {cpu['value']:.4f} GB/s ({cpu['seconds']} s)")
+
+    import torch
+    from paged_kv_cache_205_amd import ops
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load()
+    dev = "cuda"
+    log(f"workload {lay.name}: B={lay.B} layers={lay.n_layers} pool {lay.pool_bytes / 2**30:.2f} GiB, "
+        f"KV/step {lay.kv_bytes_per_step / 1e9:.3f} GB")
+    k_pool, v_pool = synth.make_pools(lay, dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
+    inputs = [synth.step_inputs(lay, l, dev) for l in range(lay.n_layers)]
+    outs = [torch.empty((lay.B, 32, 64), dtype=torch.float32, device=dev) for _ in range(lay.n_layers)]
+    part = args.partition
+    ws = ops.workspace_for(lay.B, lay.max_blocks, part, dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        for l in range(lay.n_layers):
+            x = inputs[l]
+            ops.pa_append(x["k_new"], x["v_new"], k_pool, v_pool, bt[l], seq_lens)
+            if ev is not None:
+                ev[l][0].record()
+            ops.pa_decode(x["q"], k_pool, v_pool, bt[l], seq_lens, lay.scale, out=outs[l],
+                          partition_tokens=part, workspace=ws)
+            if ev is not None:
+                ev[l][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # decode launches timed one by one (separate pass, same work)
+    dec_ms = []
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(lay.n_layers)]
+        step(ev)
+        torch.cuda.synchronize()
+        dec_ms += [a.elapsed_time(b) for a, b in ev]
+    dec_ms_mean = float(np.mean(dec_ms))
+
+    graph_ms = None
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                step()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g, stream=s):
+                    step()
+            torch.cuda.synchronize()
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            t0.record()
+            for _ in range(args.steps):
+                g.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            graph_ms = t0.elapsed_time(t1) / args.steps
+        except Exception as e:  # report, keep the stream number
+            log(f"graph capture failed: {e!r}")
+
+    kv_step = lay.kv_bytes_per_step
+    best_ms = ms_step if graph_ms is None else min(ms_step, graph_ms)
+    value = kv_step / (best_ms * 1e-3) / 1e9
+    achieved = lay.kv_bytes_per_layer / (dec_ms_mean * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(best_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{lay.name}: B={lay.B}, L={'2048' if lay.name == 'full' else 'mixed'}, "
+                        f"{lay.n_layers} layers, 32 q / 8 kv heads, D=64, 16-token BF16 pages",
+            "batch": lay.B,
+            "seq_len_max": int(lay.seq_lens.max()),
+            "layers": lay.n_layers,
+            "kv_bytes_per_step": kv_step,
+            "partition_tokens": part or ops.pa_default_partition_tokens(),
+            "timing": "graph replay" if best_ms == graph_ms else "stream launches",
+            "kv_dtype": "bf16",
+            "parallelism": "single GPU",
+        },
+        "us_per_step": round(best_ms * 1e3, 2),
+        "us_per_step_stream": round(ms_step * 1e3, 2),
+        "us_per_step_graph": None if graph_ms is None else round(graph_ms * 1e3, 2),
+        "seq_steps_per_s": round(lay.B / (best_ms * 1e-3), 1),
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "pa_decode (decode kernel + merge when splits exist)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": lay.kv_bytes_per_layer,
+            "mean_launch_us": round(dec_ms_mean * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

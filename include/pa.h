@@ -1,0 +1,170 @@
+/*
+ * pa.h - C ABI of the MI355X (gfx950) paged decode attention library (libpa.so).
+ *
+ * Sources for what is computed (web pages describing the samir-vllm teaching
+ * engine; cited by title and section):
+ *   [README] "6 Hours of YouTube and 85 handtyped pages of notes on LLM
+ *            Inference - Start here" (memedata.com copy of the project README),
+ *            feature list: the KV page pool item, the batched decode item and
+ *            the paged decode attention item.
+ *   [ARCH]   "samir-vllm: Build LLM Inference From Scratch in C++ and CUDA"
+ *            (wpnews.pro), section "Architecture walkthrough", KV cache
+ *            paragraph.
+ *   [NF]     news-factory.app article on the free LLM-inference course,
+ *            section "How does the engine manage KV cache memory?".
+ *
+ * Data model ([README] KV page pool item; [ARCH]):
+ *   - One shared BF16 pool of physical pages.  A page holds 16 tokens of K and
+ *     V of one layer.  The K plane and the V plane are two arrays indexed by
+ *     the same page id, each laid out as bf16 [num_pages][16][Hkv][D]: a token
+ *     row of one page is Hkv*D contiguous values, one KV head's row is D
+ *     contiguous values (128 bytes for D = 64).
+ *   - A block table per (sequence, layer): int32 [B][max_blocks] for one layer,
+ *     entry j is the page of logical tokens 16j .. 16j+15.  Entries at index
+ *     >= ceil(L/16) are never read (they may hold -1).
+ *   - seq_lens: int32 [B], the length of each sequence AFTER this step's
+ *     append.  One array serves every layer of a step.
+ *   - BF16 values are passed as uint16_t bit patterns.
+ *
+ * Supported model dimensions: Hkv = 8, D = 64, Hq = 32 (4 query heads per KV
+ * head).  The pages fix the model (Llama 3.2 1B, 2048-wide hidden state, 16
+ * layers, 2048-token context) but do not print the head counts; 32 x 64 = 2048
+ * is the reading used.  Other values return PA_ERR_UNSUPPORTED.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named *_pool, q, k_new, v_new, block_table, seq_lens, out,
+ *     part_* and workspace are DEVICE pointers owned by the caller.  The
+ *     library allocates, frees and synchronises nothing and keeps no state
+ *     between calls; it is reentrant.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     failed check the call returns a negative status and launches nothing.
+ *     B == 0 is a valid empty batch: the call returns PA_OK and launches
+ *     nothing.  Every array pointer must be 16-byte aligned.
+ *   - Work is enqueued on `stream` and runs asynchronously; a launch failure
+ *     reported by the runtime returns PA_ERR_LAUNCH.
+ *   - Device-side preconditions (the caller's contract, not checked):
+ *     0 <= seq_lens[b] <= 16*max_blocks; every block table entry below
+ *     ceil(L/16) lies in [0, num_pages); no two (sequence, layer) pairs own the
+ *     same page.  Slots the call does not reference may hold anything,
+ *     including NaN: they never influence a result.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_PAGE_TOKENS 16
+#define PA_HEAD_DIM 64
+#define PA_KV_HEADS 8
+#define PA_Q_HEADS 32
+#define PA_MAX_BLOCKS_LIMIT 4096
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  PA_ERR_UNSUPPORTED = -3, /* dims other than Hq=32, Hkv=8, D=64 */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
+  PA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch */
+  PA_ERR_ALIGN = -6        /* an array pointer is not 16-byte aligned */
+};
+
+/* Human-readable name of a status code (static string). */
+const char* pa_status_string(int status);
+
+/*
+ * pa_append - write this step's token of every sequence into its page slot.
+ * ([README] KV page pool item: decode appends one new token at its absolute
+ * position; [ARCH] KV cache paragraph.)
+ *
+ * For each b with L = seq_lens[b] >= 1: page = block_table[b][(L-1)/16],
+ * slot = (L-1) % 16; k_pool[page][slot][:][:] = k_new[b][:][:] and likewise
+ * v_pool from v_new, as a bit copy.  Sequences with L == 0 are skipped.
+ *
+ *   k_new, v_new  bf16 [B][Hkv][D]
+ *   k_pool, v_pool bf16 [num_pages][16][Hkv][D] (written)
+ *   block_table   int32 [B][max_blocks] of one layer
+ *   seq_lens      int32 [B]
+ * The caller assigns the page of block (L-1)/16 before the call whenever
+ * (L-1) % 16 == 0 (pages are assigned lazily by the host).
+ */
+int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
+              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+              int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
+
+/*
+ * Bytes of workspace pa_decode needs for these sizes (0 when no sequence can
+ * have more than one split).  partition_tokens = 0 selects the default.
+ * Returns 0 for invalid sizes as well; pa_decode reports those.
+ */
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
+                                 int32_t partition_tokens);
+
+/* The partition (tokens per split) pa_decode uses when passed 0. */
+int32_t pa_default_partition_tokens(void);
+
+/*
+ * pa_decode - batched paged decode attention for one layer.
+ * ([README] paged decode attention item: every query head streams its
+ * sequence's cached pages with an FP32 online softmax and accumulates V,
+ * with no contiguous gather and no stored scores; [NF].)
+ *
+ *   out[b][h][:] = sum_{t < L} softmax_t(scale * q[b][h] . K_t[g]) V_t[g],
+ *   L = seq_lens[b], g = h / (Hq/Hkv), K_t / V_t read through block_table[b].
+ *
+ *   q            bf16 [B][Hq][D] (already position-encoded)
+ *   out          fp32 [B][Hq][D]; rows of sequences with L == 0 are set to 0
+ *   scale        softmax scale (1/sqrt(D) for the model)
+ *   partition_tokens  tokens per split, a multiple of 16 (0 = default).
+ *                A sequence with L > partition_tokens is processed as
+ *                ceil(L / partition_tokens) page-aligned splits whose partial
+ *                states are combined by the merge kernel (the same kernel as
+ *                pa_merge) in the same call.  The split of a sequence depends
+ *                only on its own length, so a sequence's output does not depend
+ *                on the rest of the batch.
+ *   workspace    device buffer of at least
+ *                pa_decode_workspace_bytes(B, Hq, D, max_blocks, partition_tokens)
+ *                bytes (may be NULL when that is 0).  It holds the split
+ *                partials (part_o, part_m, part_l in the layout pa_merge takes,
+ *                with S = ceil(16*max_blocks / partition_tokens)) and is only
+ *                valid until the next call that uses it.
+ * Arithmetic: QK^T products of BF16 values are exact in FP32 and summed in
+ * FP32; softmax and accumulation are FP32; the exponentials are base 2 with
+ * log2(e) folded into the scale.
+ */
+int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, float scale,
+              float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/*
+ * pa_merge - combine split partial states into the attention output.
+ * (Split-K over page ranges is this library's own; it is exact because the
+ * log-sum-exp merge of softmax partial states is an identity.)
+ *
+ *   part_o  fp32 [B][Hq][S][D]: split s's output, already divided by its l
+ *   part_m  fp32 [B][Hq][S]: maximum over the split of x_t = scale*log2(e)*(q.K_t)
+ *   part_l  fp32 [B][Hq][S]: sum over the split of 2^(x_t - part_m)
+ *   seq_lens int32 [B] or NULL.  With seq_lens, split s of sequence b is live
+ *           iff s*partition_tokens < seq_lens[b] and sequences with L == 0
+ *           get zeros; with NULL every split is live.
+ *   out     fp32 [B][Hq][D]
+ *   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s 2^(m_s - max_s m_s), over live
+ *   splits with l_s > 0; zero if there is none.
+ */
+int pa_merge(const float* part_o, const float* part_m, const float* part_l,
+             const int32_t* seq_lens, int32_t partition_tokens, float* out, int32_t B, int32_t Hq,
+             int32_t D, int32_t S, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,175 @@
+// pa_api.cpp - the C ABI declared in include/pa.h: host-side argument checks,
+// split planning and kernel launches.  No allocation, no synchronisation.
+#include "pa.h"
+
+#include <math.h>
+
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int32_t kDefaultPartitionTokens = 256;
+constexpr size_t kAlign = 256;
+
+inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+inline size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_dims(int32_t Hq, int32_t Hkv, int32_t D) {
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || Hq % Hkv != 0) return PA_ERR_SHAPE;
+  if (Hq != pa::kQHeads || Hkv != pa::kKvHeads || D != pa::kHeadDim) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+struct Plan {
+  int32_t part_tokens;
+  int32_t part_pages;
+  int32_t S;
+  size_t off_m, off_l, bytes;
+};
+
+// Splits are page-aligned ranges of part_tokens tokens; a sequence of length L
+// has ceil(L / part_tokens) of them, independent of the rest of the batch.
+int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) {
+  if (partition_tokens < 0 || partition_tokens % pa::kPageTokens != 0) return PA_ERR_SHAPE;
+  const int32_t pt = partition_tokens == 0 ? kDefaultPartitionTokens : partition_tokens;
+  p->part_pages = pt / pa::kPageTokens;
+  if (p->part_pages >= max_blocks) p->part_pages = max_blocks;
+  p->part_tokens = p->part_pages * pa::kPageTokens;
+  p->S = (max_blocks + p->part_pages - 1) / p->part_pages;
+  if (p->S <= 1) {
+    p->S = 1;
+    p->off_m = p->off_l = p->bytes = 0;
+    return PA_OK;
+  }
+  const size_t rows = (size_t)B * pa::kQHeads * p->S;
+  p->off_m = round_up(rows * pa::kHeadDim * sizeof(float));
+  p->off_l = p->off_m + round_up(rows * sizeof(float));
+  p->bytes = p->off_l + round_up(rows * sizeof(float));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: a size or value is out of range";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: only Hq=32, Hkv=8, D=64 are built";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
+    case PA_ERR_ALIGN: return "PA_ERR_ALIGN: an array pointer is not 16-byte aligned";
+    default: return "unknown pa status";
+  }
+}
+
+int32_t pa_default_partition_tokens(void) { return kDefaultPartitionTokens; }
+
+int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
+              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+              int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream) {
+  if (B < 0 || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT || num_pages <= 0 ||
+      num_pages > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (Hkv <= 0 || D <= 0) return PA_ERR_SHAPE;
+  if (Hkv != pa::kKvHeads || D != pa::kHeadDim) return PA_ERR_UNSUPPORTED;
+  if (B == 0) return PA_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !block_table || !seq_lens) return PA_ERR_NULL;
+  if (misaligned(k_new) || misaligned(v_new) || misaligned(k_pool) || misaligned(v_pool))
+    return PA_ERR_ALIGN;
+  if (pa::launch_append(k_new, v_new, k_pool, v_pool, block_table, max_blocks, seq_lens, B,
+                        stream) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
+                                 int32_t partition_tokens) {
+  if (B <= 0 || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return 0;
+  if (check_dims(Hq, pa::kKvHeads, D) != PA_OK) return 0;
+  Plan p;
+  if (make_plan(B, max_blocks, partition_tokens, &p) != PA_OK) return 0;
+  return p.bytes;
+}
+
+int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, float scale,
+              float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  if (B < 0 || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT || num_pages <= 0 ||
+      num_pages > INT32_MAX || !isfinite(scale))
+    return PA_ERR_SHAPE;
+  const int dims = check_dims(Hq, Hkv, D);
+  if (dims != PA_OK) return dims;
+  Plan plan;
+  const int pst = make_plan(B > 0 ? B : 1, max_blocks, partition_tokens, &plan);
+  if (pst != PA_OK) return pst;
+  if (B == 0) return PA_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return PA_ERR_NULL;
+  if (misaligned(q) || misaligned(k_pool) || misaligned(v_pool) || misaligned(out))
+    return PA_ERR_ALIGN;
+  // the 1-D grid has B * Hkv * S workgroups of 64 lanes
+  if ((uint64_t)B * pa::kKvHeads * plan.S * 64 >= (1ull << 32)) return PA_ERR_SHAPE;
+  if (plan.bytes > 0) {
+    if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
+    if (misaligned(workspace)) return PA_ERR_ALIGN;
+  }
+  char* ws = static_cast<char*>(workspace);
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.part_o = plan.bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_m = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_m) : nullptr;
+  a.part_l = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.max_blocks = max_blocks;
+  a.part_pages = plan.part_pages;
+  a.S = plan.S;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  if (pa::launch_decode(a, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  if (plan.S > 1) {
+    pa::MergeArgs m;
+    m.part_o = a.part_o;
+    m.part_m = a.part_m;
+    m.part_l = a.part_l;
+    m.seq_lens = seq_lens;
+    m.out = out;
+    m.part_tokens = plan.part_tokens;
+    m.S = plan.S;
+    m.skip_single = 1;
+    if (pa::launch_merge(m, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+int pa_merge(const float* part_o, const float* part_m, const float* part_l,
+             const int32_t* seq_lens, int32_t partition_tokens, float* out, int32_t B, int32_t Hq,
+             int32_t D, int32_t S, hipStream_t stream) {
+  if (B < 0 || S <= 0 || S > PA_MAX_BLOCKS_LIMIT) return PA_ERR_SHAPE;
+  const int dims = check_dims(Hq, pa::kKvHeads, D);
+  if (dims != PA_OK) return dims;
+  if (seq_lens && (partition_tokens <= 0 || partition_tokens % pa::kPageTokens != 0))
+    return PA_ERR_SHAPE;
+  if (B == 0) return PA_OK;
+  if (!part_o || !part_m || !part_l || !out) return PA_ERR_NULL;
+  if (misaligned(part_o) || misaligned(out)) return PA_ERR_ALIGN;
+  pa::MergeArgs m;
+  m.part_o = part_o;
+  m.part_m = part_m;
+  m.part_l = part_l;
+  m.seq_lens = seq_lens;
+  m.out = out;
+  m.part_tokens = seq_lens ? partition_tokens : 0;
+  m.S = S;
+  m.skip_single = 0;
+  if (pa::launch_merge(m, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+"""Thin ctypes binding over libpa.so (the C ABI of include/pa.h).
+
+Argument marshalling only: torch tensors become device pointers and the current
+HIP stream becomes the ``hipStream_t``; every step of the computation runs in
+the library's kernels.  If the library is missing the calls raise; there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+PA_OK = 0
+STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
+          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN"}
+EXPORTS = ("pa_status_string", "pa_append", "pa_decode_workspace_bytes",
+           "pa_default_partition_tokens", "pa_decode", "pa_merge")
+
+_lib = None
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} returned {status} ({text})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load libpa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with paged_kv_cache_205_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_append.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I64, P]
+    lib.pa_append.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.pa_decode_workspace_bytes.restype = SZ
+    lib.pa_default_partition_tokens.argtypes = []
+    lib.pa_default_partition_tokens.restype = I32
+    lib.pa_decode.argtypes = [P, P, P, P, I32, P, F32, P, I32, I32, I32, I32, I64, I32, P, SZ, P]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_merge.argtypes = [P, P, P, P, I32, P, I32, I32, I32, I32, P]
+    lib.pa_merge.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != PA_OK:
+        raise PAError(fn, status, load().pa_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype, name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _bf16(t, name):
+    return _ptr(t, torch.bfloat16, name)
+
+
+def pa_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, stream=None) -> None:
+    """k_new/v_new bf16 [B][8][64]; pools bf16 [num_pages][16][8][64]; block_table int32 [B][max_blocks]."""
+    B, Hkv, D = k_new.shape
+    lib = load()
+    st = lib.pa_append(_bf16(k_new, "k_new"), _bf16(v_new, "v_new"), _bf16(k_pool, "k_pool"),
+                       _bf16(v_pool, "v_pool"), _ptr(block_table, torch.int32, "block_table"),
+                       block_table.shape[1], _ptr(seq_lens, torch.int32, "seq_lens"), B, Hkv, D,
+                       k_pool.shape[0], _stream(k_pool.device, stream))
+    _check("pa_append", st)
+
+
+def pa_decode_workspace_bytes(B: int, max_blocks: int, partition_tokens: int = 0, Hq: int = 32, D: int = 64) -> int:
+    return int(load().pa_decode_workspace_bytes(B, Hq, D, max_blocks, partition_tokens))
+
+
+def pa_default_partition_tokens() -> int:
+    return int(load().pa_default_partition_tokens())
+
+
+def workspace_for(B: int, max_blocks: int, partition_tokens: int = 0, device="cuda") -> Optional[torch.Tensor]:
+    n = pa_decode_workspace_bytes(B, max_blocks, partition_tokens)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None,
+              partition_tokens: int = 0, workspace=None, stream=None) -> torch.Tensor:
+    """q bf16 [B][32][64] -> out fp32 [B][32][64] (allocated if not given)."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(B, block_table.shape[1], partition_tokens, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib = load()
+    st = lib.pa_decode(_bf16(q, "q"), _bf16(k_pool, "k_pool"), _bf16(v_pool, "v_pool"),
+                       _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+                       _ptr(seq_lens, torch.int32, "seq_lens"), float(scale),
+                       _ptr(out, torch.float32, "out"), B, Hq, Hkv, D, k_pool.shape[0],
+                       partition_tokens, ws_ptr, ws_n, _stream(q.device, stream))
+    _check("pa_decode", st)
+    return out
+
+
+def pa_merge(part_o, part_m, part_l, seq_lens=None, partition_tokens: int = 0, out=None, stream=None):
+    """part_o fp32 [B][32][S][64], part_m / part_l fp32 [B][32][S] (base-2 maxima) -> out fp32 [B][32][64]."""
+    B, Hq, S, D = part_o.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=part_o.device)
+    lib = load()
+    st = lib.pa_merge(_ptr(part_o, torch.float32, "part_o"), _ptr(part_m, torch.float32, "part_m"),
+                      _ptr(part_l, torch.float32, "part_l"),
+                      _ptr(seq_lens, torch.int32, "seq_lens") if seq_lens is not None else None,
+                      partition_tokens, _ptr(out, torch.float32, "out"), B, Hq, D, S,
+                      _stream(part_o.device, stream))
+    _check("pa_merge", st)
+    return out

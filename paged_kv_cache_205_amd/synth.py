@@ -284,6 +284,12 @@ def step_inputs(lay: Layout, layer: int, device="cpu") -> Dict[str, torch.Tensor
     }
 
 
+def _layer_values(lay: Layout, l: int, n: int, c: int, dev) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Values of chunk c (n token rows) of layer l's pre-filled positions."""
+    return (_randn_bf16((n, ROW_ELEMS), lay.sigma_k, dev, _torch_seed(lay.config_id, lay.draw, _S_K, (l << 16) | c)),
+            _randn_bf16((n, ROW_ELEMS), lay.sigma_v, dev, _torch_seed(lay.config_id, lay.draw, _S_V, (l << 16) | c)))
+
+
 def make_pools(lay: Layout, device="cpu", layers: Optional[List[int]] = None,
                chunk_rows: int = 1 << 22) -> Tuple[torch.Tensor, torch.Tensor]:
     """K and V planes, bf16 [num_pages][16][8][64], NaN everywhere except positions 0..L-2.
@@ -302,12 +308,34 @@ def make_pools(lay: Layout, device="cpu", layers: Optional[List[int]] = None,
         rows = torch.from_numpy(pages * PAGE_TOKENS + slots).to(dev)
         for c, start in enumerate(range(0, len(rows), chunk_rows)):
             r = rows[start:start + chunk_rows]
-            n = r.numel()
-            kf[r] = _randn_bf16((n, ROW_ELEMS), lay.sigma_k, dev,
-                                _torch_seed(lay.config_id, lay.draw, _S_K, (l << 16) | c))
-            vf[r] = _randn_bf16((n, ROW_ELEMS), lay.sigma_v, dev,
-                                _torch_seed(lay.config_id, lay.draw, _S_V, (l << 16) | c))
+            kf[r], vf[r] = _layer_values(lay, l, r.numel(), c, dev)
     return k_pool, v_pool
+
+
+def layer_pages(lay: Layout, layer: int, device="cpu", chunk_rows: int = 1 << 22):
+    """Only the pages of one layer, renumbered 0..n-1: (k_pages, v_pages, block_table).
+
+    Holds the same values ``make_pools`` puts in those pages (same generators,
+    same order), without materialising the rest of the pool.  The returned
+    block table is int32 [B][max_blocks] in the local numbering (-1 kept).
+    """
+    dev = torch.device(device)
+    bt = lay.block_tables[layer]
+    used = np.unique(np.concatenate([bt[b, :nblocks(lay.seq_lens[b])] for b in range(lay.B)] or [np.zeros(0, np.int32)]))
+    local = np.full(lay.num_pages, -1, np.int64)
+    local[used] = np.arange(len(used))
+    bt_local = np.where(bt >= 0, local[np.maximum(bt, 0)], -1).astype(np.int32)
+    shape = (len(used), PAGE_TOKENS, HKV, HEAD_DIM)
+    k_pages = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pages = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    kf = k_pages.view(-1, ROW_ELEMS)
+    vf = v_pages.view(-1, ROW_ELEMS)
+    pages, slots = lay.filled_slots(layer)
+    rows = torch.from_numpy(local[pages] * PAGE_TOKENS + slots).to(dev)
+    for c, start in enumerate(range(0, len(rows), chunk_rows)):
+        r = rows[start:start + chunk_rows]
+        kf[r], vf[r] = _layer_values(lay, layer, r.numel(), c, dev)
+    return k_pages, v_pages, bt_local
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI) against the FP64 oracle.
+
+Append: bit-exact (whole pool compared).  Decode: no NaN/Inf, max abs error
+<= 2e-3 and row-wise relative error <= 1e-2 against the oracle, on the five
+workloads (tiny and small in full; reduced copies of the others in full; the
+full-size ones on sampled sequences plus properties of every output).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import append_ref, bf16_to_f64, decode_ref, partial_ref
+from paged_kv_cache_205_amd import ops, synth
+from tests.helpers import Device, check_close, oracle_sequence, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.load()
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def host(t):
+    return synth.bits(t)
+
+
+# ---------------------------------------------------------------- tiny and small, in full
+
+
+def test_tiny_decode_append_decode():
+    lay = synth.tiny()
+    d = Device(lay)
+    bt = lay.block_tables[0]
+    kp0, vp0 = host(d.k_pool), host(d.v_pool)
+    q = host(d.inputs[0]["q"])
+    sl37 = torch.tensor([37], dtype=torch.int32, device="cuda")
+    out37 = d.decode(0, seq_lens=sl37).cpu().numpy()
+    check_close(out37, decode_ref(q, kp0, vp0, bt, np.array([37]), lay.scale), "tiny L=37")
+    d.append(0)
+    k2, v2 = append_ref(kp0, vp0, host(d.inputs[0]["k_new"]), host(d.inputs[0]["v_new"]), bt, lay.seq_lens)
+    assert np.array_equal(host(d.k_pool), k2) and np.array_equal(host(d.v_pool), v2)
+    out38 = d.decode(0).cpu().numpy()
+    ea, er = check_close(out38, decode_ref(q, k2, v2, bt, lay.seq_lens, lay.scale), "tiny L=38")
+    say(f"tiny: max abs {ea:.2e} rel {er:.2e}")
+
+
+def test_small_all_layers():
+    lay = synth.small()
+    d = Device(lay)
+    worst = 0.0
+    for l in range(lay.n_layers):
+        kp0, vp0 = host(d.k_pool), host(d.v_pool)
+        x = d.inputs[l]
+        d.append(l)
+        torch.cuda.synchronize()
+        k2, v2 = append_ref(kp0, vp0, host(x["k_new"]), host(x["v_new"]), lay.block_tables[l], lay.seq_lens)
+        assert np.array_equal(host(d.k_pool), k2), f"layer {l}: K pool differs after append"
+        assert np.array_equal(host(d.v_pool), v2), f"layer {l}: V pool differs after append"
+        out = d.decode(l).cpu().numpy()
+        ref = decode_ref(host(x["q"]), k2, v2, lay.block_tables[l], lay.seq_lens, lay.scale)
+        worst = max(worst, check_close(out, ref, f"small layer {l}")[0])
+    say(f"small: 16 layers, worst max abs {worst:.2e}")
+
+
+# ---------------------------------------------------------------- reduced copies, in full
+
+
+REDUCED = [
+    ("fragmented", lambda: synth.fragmented(B=24, n_layers=2)),
+    ("skewed", lambda: synth.skewed(B=48, n_layers=2)),
+    ("large", lambda: synth.large(B=10, n_layers=2)),
+    ("full", lambda: synth.full(B=3, n_layers=2)),
+]
+
+
+@pytest.mark.parametrize("partition", [0, 16, 64, 256, 2048])
+@pytest.mark.parametrize("name,make", REDUCED, ids=[r[0] for r in REDUCED])
+def test_reduced_configs_in_full(name, make, partition):
+    lay = make()
+    d = Device(lay)
+    for l in range(lay.n_layers):
+        kp0, vp0 = host(d.k_pool), host(d.v_pool)
+        x = d.inputs[l]
+        d.append(l)
+        k2, v2 = append_ref(kp0, vp0, host(x["k_new"]), host(x["v_new"]), lay.block_tables[l], lay.seq_lens)
+        assert np.array_equal(host(d.k_pool), k2) and np.array_equal(host(d.v_pool), v2)
+        out = d.decode(l, partition_tokens=partition).cpu().numpy()
+        ref = decode_ref(host(x["q"]), k2, v2, lay.block_tables[l], lay.seq_lens, lay.scale)
+        ea, er = check_close(out, ref, f"{lay.name} layer {l} partition {partition}")
+    say(f"{lay.name} partition {partition}: max abs {ea:.2e} rel {er:.2e}")
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+
+
+def _sample(lay: synth.Layout):
+    L = lay.seq_lens
+    picks = {int(np.argmax(L)), int(np.argmin(L)), 0, lay.B - 1}
+    picks |= {int(i) for i in np.nonzero(L % 16 == 1)[0][:1]} | {int(i) for i in np.nonzero(L % 16 == 0)[0][:1]}
+    rng = np.random.default_rng(7)
+    picks |= {int(i) for i in rng.integers(0, lay.B, size=2)}
+    layers = sorted({0, lay.n_layers - 1, lay.n_layers // 2})
+    return [(l, b) for l in layers for b in sorted(picks)]
+
+
+@pytest.mark.parametrize("name", ["full", "fragmented", "skewed", "large"])
+def test_full_size_sampled(name):
+    lay = synth.get(name)
+    say(f"{name}: B={lay.B} layers={lay.n_layers} pool {lay.pool_bytes / 2**30:.2f} GiB")
+    d = Device(lay)
+    sample = _sample(lay)
+    pages = {lb: synth.sequence_pages(d.k_pool, d.v_pool, lay, *lb) for lb in sample}
+    k_before, v_before = d.k_pool.clone(), d.v_pool.clone()
+    outs = []
+    for l in range(lay.n_layers):
+        d.append(l)
+        outs.append(d.decode(l))
+    torch.cuda.synchronize()
+    # append: exactly the 2B target rows of every layer changed, to the k_new/v_new bits
+    kf = k_before.view(-1, synth.ROW_ELEMS)
+    vf = v_before.view(-1, synth.ROW_ELEMS)
+    Lm1 = lay.seq_lens.astype(np.int64) - 1
+    for l in range(lay.n_layers):
+        live = np.nonzero(Lm1 >= 0)[0]
+        rows = lay.block_tables[l, live, Lm1[live] // 16].astype(np.int64) * 16 + Lm1[live] % 16
+        r = torch.from_numpy(rows).cuda()
+        idx = torch.from_numpy(live).cuda()
+        kf[r] = d.inputs[l]["k_new"].view(lay.B, -1)[idx]
+        vf[r] = d.inputs[l]["v_new"].view(lay.B, -1)[idx]
+    assert torch.equal(k_before.view(torch.int16), d.k_pool.view(torch.int16)), "K pool differs"
+    assert torch.equal(v_before.view(torch.int16), d.v_pool.view(torch.int16)), "V pool differs"
+    del k_before, v_before, kf, vf
+    # every output finite; each output is a convex combination of V rows
+    vmax = 0.0
+    for p0 in range(0, lay.num_pages, 1 << 15):
+        chunk = d.v_pool[p0:p0 + (1 << 15)].float().abs()
+        vmax = max(vmax, float(torch.nan_to_num(chunk, nan=0.0).max()))
+    for l, o in enumerate(outs):
+        assert bool(torch.isfinite(o).all()), f"layer {l}: non-finite output"
+        assert float(o.abs().max()) <= vmax
+    worst = 0.0
+    for (l, b) in sample:
+        kp, vp, _ = pages[(l, b)]
+        ref = oracle_sequence(d, l, b, kp, vp)
+        got = outs[l][b].cpu().numpy()
+        worst = max(worst, check_close(got, ref, f"{name} layer {l} seq {b} (L={lay.seq_lens[b]})")[0])
+    say(f"{name}: {len(sample)} sampled sequences, worst max abs {worst:.2e}")
+
+
+# ---------------------------------------------------------------- invariants on the GPU
+
+
+def test_page_permutation_bit_identical():
+    lay = synth.small()
+    d = Device(lay)
+    for l in range(2):
+        d.append(l)
+    base = [d.decode(l, partition_tokens=p).clone() for l in range(2) for p in (0, 64)]
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(lay.num_pages)).cuda()
+    kq = torch.empty_like(d.k_pool)
+    vq = torch.empty_like(d.v_pool)
+    kq[perm] = d.k_pool
+    vq[perm] = d.v_pool
+    bt2 = torch.where(d.bt >= 0, perm[d.bt.clamp(min=0).long()].int(), d.bt)
+    d.k_pool, d.v_pool, d.bt = kq, vq, bt2.contiguous()
+    again = [d.decode(l, partition_tokens=p) for l in range(2) for p in (0, 64)]
+    for x, y in zip(base, again):
+        assert torch.equal(x, y)
+
+
+def test_batch_invariance():
+    lay = synth.fragmented(B=16, n_layers=1)
+    d = Device(lay)
+    d.append(0)
+    full = d.decode(0)
+    x = d.inputs[0]
+    for b in (0, 3, 7, 15):
+        sub = ops.pa_decode(x["q"][b:b + 1].contiguous(), d.k_pool, d.v_pool, d.bt[0][b:b + 1].contiguous(),
+                            d.seq_lens[b:b + 1].contiguous(), lay.scale)
+        assert torch.equal(sub[0], full[b]), f"sequence {b} changes with the batch"
+
+
+def test_split_results_agree():
+    lay = synth.fragmented(B=12, n_layers=1)
+    d = Device(lay)
+    d.append(0)
+    outs = {p: d.decode(0, partition_tokens=p).clone() for p in (16, 64, 256, 2048)}
+    for p in (16, 64, 256):
+        assert float((outs[p] - outs[2048]).abs().max()) <= 2e-3
+
+
+def test_length_one_is_the_v_row():
+    lay = synth.small()
+    L1 = torch.ones(lay.B, dtype=torch.int32, device="cuda")
+    d = Device(lay)
+    d.append(0, seq_lens=L1)
+    out = d.decode(0, seq_lens=L1)
+    v = d.inputs[0]["v_new"].float()  # position 0 is the appended row
+    want = v.repeat_interleave(4, dim=1)
+    assert torch.equal(out, want)
+
+
+def test_gqa_isolation():
+    lay = synth.fragmented(B=8, n_layers=1)
+    d = Device(lay)
+    d.append(0)
+    base = d.decode(0).clone()
+    for g in (0, 5):
+        kq, vq = d.k_pool.clone(), d.v_pool.clone()
+        others = [x for x in range(8) if x != g]
+        kq[:, :, others] = float("nan")
+        vq[:, :, others] = float("nan")
+        out = ops.pa_decode(d.inputs[0]["q"], kq, vq, d.bt[0], d.seq_lens, lay.scale)
+        assert torch.equal(out[:, 4 * g:4 * g + 4], base[:, 4 * g:4 * g + 4])
+
+
+def test_empty_sequences_and_empty_batch():
+    lay = synth.fragmented(B=8, n_layers=1)
+    d = Device(lay)
+    d.append(0)
+    sl = d.seq_lens.clone()
+    sl[[1, 6]] = 0
+    for p in (0, 64):
+        out = torch.full((8, 32, 64), float("nan"), device="cuda")
+        d.decode(0, partition_tokens=p, seq_lens=sl, out=out)
+        assert bool((out[[1, 6]] == 0).all())
+        full = d.decode(0, partition_tokens=p)
+        assert torch.equal(out[[0, 2, 3, 4, 5, 7]], full[[0, 2, 3, 4, 5, 7]])
+    # B = 0 launches nothing
+    e = torch.empty((0, 32, 64), dtype=torch.bfloat16, device="cuda")
+    ops.pa_decode(e, d.k_pool, d.v_pool, d.bt[0][:0].contiguous(), d.seq_lens[:0].contiguous(), 0.125)
+    ops.pa_append(e[:, :8].contiguous(), e[:, :8].contiguous(), d.k_pool, d.v_pool, d.bt[0][:0].contiguous(),
+                  d.seq_lens[:0].contiguous())
+
+
+def test_merge_standalone_against_oracle_partials():
+    lay = synth.fragmented(B=6, n_layers=1)
+    k, v = synth.make_pools(lay, "cpu")
+    x = synth.step_inputs(lay, 0, "cpu")
+    kp, vp, q = host(k), host(v), host(x["q"])
+    bt = lay.block_tables[0]
+    # partial states are over the pre-filled positions only (L-1 tokens)
+    sl = np.maximum(lay.seq_lens - 1, 0).astype(np.int32)
+    part = 128
+    S = 16
+    B = lay.B
+    po = np.zeros((B, 32, S, 64), np.float32)
+    pm = np.zeros((B, 32, S), np.float32)
+    pl = np.zeros((B, 32, S), np.float32)
+    for b in range(B):
+        for h in range(32):
+            for s in range(S):
+                t0, t1 = s * part, min(int(sl[b]), (s + 1) * part)
+                if t0 >= t1:
+                    continue
+                m, l, o = partial_ref(q, kp, vp, bt, sl, lay.scale, b, h, t0, t1)
+                pm[b, h, s] = m * math.log2(math.e)
+                pl[b, h, s] = l
+                po[b, h, s] = o
+    ref = decode_ref(q, kp, vp, bt, sl, lay.scale)
+    dev = lambda a: torch.from_numpy(a).cuda()
+    out = ops.pa_merge(dev(po), dev(pm), dev(pl), dev(sl), part).cpu().numpy()
+    check_close(out, ref, "pa_merge with seq_lens")
+    out2 = ops.pa_merge(dev(po), dev(pm), dev(pl)).cpu().numpy()  # all splits live; empty ones have l = 0
+    check_close(out2, ref, "pa_merge without seq_lens")

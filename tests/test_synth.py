@@ -77,3 +77,16 @@ def test_sigma_k_three():
     p, s = lay.filled_slots(0)
     x = k[torch.from_numpy(p), torch.from_numpy(s)].float()
     assert abs(x.std().item() - 3.0) < 0.1
+
+
+def test_layer_pages_match_make_pools():
+    lay = synth.fragmented(B=12, n_layers=3)
+    k, v = synth.make_pools(lay, "cpu")
+    for l in range(3):
+        kl, vl, btl = synth.layer_pages(lay, l, "cpu")
+        for b in range(lay.B):
+            n = synth.nblocks(lay.seq_lens[b])
+            assert torch.equal(k[torch.from_numpy(lay.block_tables[l, b, :n].astype(np.int64))].view(torch.int16),
+                               kl[torch.from_numpy(btl[b, :n].astype(np.int64))].view(torch.int16))
+            assert torch.equal(v[torch.from_numpy(lay.block_tables[l, b, :n].astype(np.int64))].view(torch.int16),
+                               vl[torch.from_numpy(btl[b, :n].astype(np.int64))].view(torch.int16))
