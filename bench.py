@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the workload the oracle runs on")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -143,6 +145,11 @@ def main():
     outs = [torch.empty((lay.B, 32, 64), dtype=torch.float32, device=dev) for _ in range(lay.n_layers)]
     part = args.partition
     ws = ops.workspace_for(lay.B, lay.max_blocks, part, dev)
+    if args.calib_copy_mib:
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        del src, dst
     torch.cuda.synchronize()
 
     def step(ev=None):

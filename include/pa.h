@@ -121,11 +121,13 @@ int32_t pa_default_partition_tokens(void);
  *   q            bf16 [B][Hq][D] (already position-encoded)
  *   out          fp32 [B][Hq][D]; rows of sequences with L == 0 are set to 0
  *   scale        softmax scale (1/sqrt(D) for the model)
- *   partition_tokens  tokens per split, a multiple of 16 (0 = default).
- *                A sequence with L > partition_tokens is processed as
- *                ceil(L / partition_tokens) page-aligned splits whose partial
+ *   partition_tokens  split size in tokens, a multiple of 16 (0 = default,
+ *                pa_default_partition_tokens(); values above 2048 act as 2048).
+ *                A sequence of L tokens (npages = ceil(L/16) pages) is processed
+ *                as S_b = ceil(L / partition_tokens) splits; split s takes the
+ *                pages s, s + S_b, s + 2 S_b, ...  When S_b > 1 the partial
  *                states are combined by the merge kernel (the same kernel as
- *                pa_merge) in the same call.  The split of a sequence depends
+ *                pa_merge) in the same call.  The splits of a sequence depend
  *                only on its own length, so a sequence's output does not depend
  *                on the rest of the batch.
  *   workspace    device buffer of at least
@@ -153,8 +155,10 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
  *   part_m  fp32 [B][Hq][S]: maximum over the split of x_t = scale*log2(e)*(q.K_t)
  *   part_l  fp32 [B][Hq][S]: sum over the split of 2^(x_t - part_m)
  *   seq_lens int32 [B] or NULL.  With seq_lens, split s of sequence b is live
- *           iff s*partition_tokens < seq_lens[b] and sequences with L == 0
- *           get zeros; with NULL every split is live.
+ *           iff s*partition_tokens < seq_lens[b] (the splits pa_decode makes)
+ *           and sequences with L == 0 get zeros; with NULL every split is live.
+ *   A split's token set does not matter to the merge: any partition of a
+ *   sequence's tokens into splits gives the same result.
  *   out     fp32 [B][Hq][D]
  *   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s 2^(m_s - max_s m_s), over live
  *   splits with l_s > 0; zero if there is none.

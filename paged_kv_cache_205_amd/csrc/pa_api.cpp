@@ -8,7 +8,8 @@
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 256;
+constexpr int32_t kDefaultPartitionTokens = 512;
+constexpr int32_t kMaxPartitionTokens = 2048;  // a split holds at most 128 pages
 constexpr size_t kAlign = 256;
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -27,11 +28,12 @@ struct Plan {
   size_t off_m, off_l, bytes;
 };
 
-// Splits are page-aligned ranges of part_tokens tokens; a sequence of length L
-// has ceil(L / part_tokens) of them, independent of the rest of the batch.
+// A sequence of length L has ceil(L / part_tokens) splits (each a set of pages),
+// independent of the rest of the batch.
 int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) {
   if (partition_tokens < 0 || partition_tokens % pa::kPageTokens != 0) return PA_ERR_SHAPE;
-  const int32_t pt = partition_tokens == 0 ? kDefaultPartitionTokens : partition_tokens;
+  int32_t pt = partition_tokens == 0 ? kDefaultPartitionTokens : partition_tokens;
+  if (pt > kMaxPartitionTokens) pt = kMaxPartitionTokens;
   p->part_pages = pt / pa::kPageTokens;
   if (p->part_pages >= max_blocks) p->part_pages = max_blocks;
   p->part_tokens = p->part_pages * pa::kPageTokens;
@@ -111,8 +113,8 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return PA_ERR_NULL;
   if (misaligned(q) || misaligned(k_pool) || misaligned(v_pool) || misaligned(out))
     return PA_ERR_ALIGN;
-  // the 1-D grid has B * Hkv * S workgroups of 64 lanes
-  if ((uint64_t)B * pa::kKvHeads * plan.S * 64 >= (1ull << 32)) return PA_ERR_SHAPE;
+  // the 1-D grid has B * S workgroups of 512 lanes
+  if ((uint64_t)B * plan.S * 512 >= (1ull << 32)) return PA_ERR_SHAPE;
   if (plan.bytes > 0) {
     if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
     if (misaligned(workspace)) return PA_ERR_ALIGN;
@@ -135,6 +137,7 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
   if (pa::launch_decode(a, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
   if (plan.S > 1) {
     pa::MergeArgs m;
+    m.B = B;
     m.part_o = a.part_o;
     m.part_m = a.part_m;
     m.part_l = a.part_l;
@@ -143,7 +146,7 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
     m.part_tokens = plan.part_tokens;
     m.S = plan.S;
     m.skip_single = 1;
-    if (pa::launch_merge(m, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
+    if (pa::launch_merge(m, stream) != hipSuccess) return PA_ERR_LAUNCH;
   }
   return PA_OK;
 }
@@ -160,6 +163,7 @@ int pa_merge(const float* part_o, const float* part_m, const float* part_l,
   if (!part_o || !part_m || !part_l || !out) return PA_ERR_NULL;
   if (misaligned(part_o) || misaligned(out)) return PA_ERR_ALIGN;
   pa::MergeArgs m;
+  m.B = B;
   m.part_o = part_o;
   m.part_m = part_m;
   m.part_l = part_l;
@@ -168,7 +172,8 @@ int pa_merge(const float* part_o, const float* part_m, const float* part_l,
   m.part_tokens = seq_lens ? partition_tokens : 0;
   m.S = S;
   m.skip_single = 0;
-  if (pa::launch_merge(m, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  if ((uint64_t)B * pa::kQHeads * 16 >= (1ull << 32)) return PA_ERR_SHAPE;
+  if (pa::launch_merge(m, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -26,12 +26,13 @@ struct DecodeArgs {
   float* part_m;  // [B][Hq][S]
   float* part_l;  // [B][Hq][S]
   int max_blocks;
-  int part_pages;  // pages per split
-  int S;           // splits per sequence in the grid = ceil(max_blocks / part_pages)
+  int part_pages;    // a sequence of npages pages has ceil(npages / part_pages) splits (part_pages <= 128)
+  int S;             // splits per sequence in the grid = ceil(max_blocks / part_pages)
   float scale_log2;  // scale * log2(e)
 };
 
 struct MergeArgs {
+  int B;
   const float* part_o;
   const float* part_m;
   const float* part_l;
@@ -46,6 +47,6 @@ hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t*
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int B, hipStream_t stream);
-hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace pa

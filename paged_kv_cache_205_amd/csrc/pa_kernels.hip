@@ -11,7 +11,7 @@
 //
 // Pool plane layout: bf16 [num_pages][16 tokens][8 kv heads][64].  One token row
 // of a page is 1 KiB; one (token, kv head) row is 128 contiguous bytes, so the
-// 16 rows a kv head reads from a page are 16 full 128-byte lines.
+// K (or V) tile of one kv head in one page is 16 full 128-byte lines.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,41 +20,30 @@
 namespace pa {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// DPP row rotations (within each row of 16 lanes).
-#define PA_DPP_ROR(n) (0x120 + (n))
-
-template <int CTRL>
-__device__ __forceinline__ float ror16(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
-}
-
-// All-reduce over the 16 lanes of a row: every lane ends with the row's max / sum.
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, ror16<PA_DPP_ROR(8)>(x));
-  x = fmaxf(x, ror16<PA_DPP_ROR(4)>(x));
-  x = fmaxf(x, ror16<PA_DPP_ROR(2)>(x));
-  x = fmaxf(x, ror16<PA_DPP_ROR(1)>(x));
-  return x;
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += ror16<PA_DPP_ROR(8)>(x);
-  x += ror16<PA_DPP_ROR(4)>(x);
-  x += ror16<PA_DPP_ROR(2)>(x);
-  x += ror16<PA_DPP_ROR(1)>(x);
-  return x;
-}
-
-__device__ __forceinline__ float bf16_lo(unsigned w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(unsigned w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0): all LDS (and scalar) reads of this wave have returned.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+__device__ __forceinline__ float lane_read(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+
 // ---------------------------------------------------------------------------
 // pa_append: one wave per sequence; each lane copies 16 bytes of the 1 KiB K
-// row and 16 bytes of the 1 KiB V row.
+// row and 16 bytes of the 1 KiB V row of position L-1.
 
 __global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict__ k_new,
                                                      const uint16_t* __restrict__ v_new,
@@ -77,194 +66,245 @@ __global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// pa_decode: one wave per work item (sequence b, kv head g, split s).
+// pa_decode
 //
-// Lane l = 16*c + t: token t (0..15) of the current page, dim chunk c (0..3).
-// The lane loads 16 bytes of K (dims 8c..8c+7) and 16 bytes at +64 B (dims
-// 32+8c..32+8c+7) of row (t, g), and the same 32 bytes of V.
+// Work decomposition.  A sequence of npages pages is cut into
+// nsplit = ceil(npages / part_pages) splits; split s owns the pages
+// s, s + nsplit, s + 2*nsplit, ... (pages are dealt round-robin, so the
+// workgroups of one sequence stream neighbouring pages at the same time).  The
+// split count depends only on the sequence's own length.  One workgroup of 8
+// waves handles one (sequence, split); wave g handles kv head g, i.e. query
+// heads 4g..4g+3, so each page's K and V are read once for the 4 query heads
+// that share them, and the 8 waves together read whole pages.
 //
-// QK^T runs on the matrix cores: S^T tile via two v_mfma_f32_16x16x32_bf16,
-// A = the 4 query heads of group g repeated to 16 rows (row i -> head i % 4),
-// B = the K tile (column j = token j).  Lane l then holds s[h = r][t = l % 16]
-// in result register r, in every row c, which is exactly the token this lane
-// holds V for.  BF16 x BF16 products are exact in FP32; sums are FP32.
+// Memory path.  Each wave streams its head's 2 KiB K tile and 2 KiB V tile of a
+// page straight into its own LDS ring slot with global_load_lds_dwordx4
+// (non-temporal): every load instruction covers 8 complete 128-byte lines.
+// Inside a tile, token row tau keeps its eight 16-byte chunks in a permuted order
+// (chunk C at position C ^ swz(tau)) so that the reads below are bank-conflict
+// free.  kRing slots per wave keep kRing pages in flight.
 //
-// Softmax is online (FP32): a running maximum per head, shared by the wave, is
-// raised only when some score exceeds it (then acc and l are rescaled); the
-// weights p = 2^(x - m) with x = scale*log2(e)*(q.k).  PV runs on the VALU in
-// FP32: acc[h][i] += p[h] * V[t][dim i of chunk c].  Each lane accumulates its
-// own tokens; the 16 lanes of a row are summed once per work item (DPP).
+// Arithmetic (per page, per wave).
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (two, for D = 64): A = K tile
+//   (row = token), B = Q^T with the 4 query heads repeated over the 16 columns.
+//   Lane l = 16c + t then holds, in result register r, the score of token
+//   4c + r for query head t % 4.  BF16 x BF16 products are exact in FP32.
+//   Online softmax in FP32 (base 2, log2(e) folded into the scale): a running
+//   maximum per head, the same in every lane of that head, is raised only when
+//   a score exceeds it (then the accumulators are rescaled).
+//   PV on v_mfma_f32_16x16x16_bf16: A = the weights of the lane's 4 tokens for
+//   its head, B = V transposed (read as 16-bit elements from the LDS tile).
+//   The FP32 weight p is split into p_hi = bf16 truncation of p and
+//   p_lo = bf16 truncation of (p - p_hi); two MFMAs accumulate p_hi V + p_lo V
+//   in FP32, which represents p to about 2^-14 relative.  Result register r of
+//   tile n holds out[head r][16n + t].
 
-constexpr int kPrefetch = 2;  // pages loaded ahead of the one being consumed
+constexpr int kRing = 2;                                 // LDS slots (pages in flight) per wave
+constexpr int kTileBytes = kPageTokens * kHeadDim * 2;   // one head's K or V rows of a page
+constexpr int kSlotBytes = 2 * kTileBytes;               // K tile then V tile
 
-struct PageRegs {
-  u32x4 k0, k1, v0, v1;
-};
+// Position permutation of the 16-byte chunks inside LDS token row tau.
+__device__ __forceinline__ int swz(int tau) { return (tau & 7) ^ ((tau >> 3) << 1); }
 
-__device__ __forceinline__ void load_page(PageRegs& r, const uint16_t* __restrict__ k_pool,
-                                          const uint16_t* __restrict__ v_pool, int32_t page,
-                                          uint32_t loff) {
-  const size_t base = (size_t)(uint32_t)page * (size_t)(kPageTokens * kRowElems) + loff;
-  r.k0 = ld16(k_pool + base);
-  r.k1 = ld16(k_pool + base + 32);
-  r.v0 = ld16(v_pool + base);
-  r.v1 = ld16(v_pool + base + 32);
-}
+__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char ring[kKvHeads][kRing][kSlotBytes];
 
-__global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  // 1-D grid: blockIdx.x = (b * Hkv + g) * S + split
-  const int split = blockIdx.x % a.S;
-  const int bg = blockIdx.x / a.S;
-  const int g = bg % kKvHeads;
-  const int b = bg / kKvHeads;
-  const int lane = threadIdx.x;
+  const int s = blockIdx.x % a.S;
+  const int b = blockIdx.x / a.S;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int t = lane & 15;
   const int c = lane >> 4;
 
   const int L = a.seq_lens[b];
-  const int npages = (L + kPageTokens - 1) / kPageTokens;
-  const int p0 = split * a.part_pages;
-  if (p0 >= npages) {
-    if (L <= 0 && split == 0) {  // empty sequence: zero output rows of this group
-      float* o = a.out + ((size_t)b * kQHeads + g * kGroup) * kHeadDim;
-      reinterpret_cast<f32x4*>(o)[lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+  if (L <= 0) {  // empty sequence: zero its output rows (split 0 only)
+    if (s == 0)
+      reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup) * kHeadDim)[lane] =
+          f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
-  const int p1 = min(p0 + a.part_pages, npages);
+  const int npages = (L + kPageTokens - 1) / kPageTokens;
+  const int nsplit = (npages + a.part_pages - 1) / a.part_pages;
+  if (s >= nsplit) return;
+  const int n = (npages - s + nsplit - 1) / nsplit;  // pages s, s + nsplit, ... (n <= part_pages <= 128)
 
-  // A operand: query head 4g + (t % 4), dims 8c..8c+7 and 32+8c..32+8c+7.
-  const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
-  const bf16x8 qa0 = __builtin_bit_cast(bf16x8, ld16(qrow + 8 * c));
-  const bf16x8 qa1 = __builtin_bit_cast(bf16x8, ld16(qrow + 32 + 8 * c));
-
-  const uint32_t loff = (uint32_t)(t * kRowElems + g * kHeadDim + 8 * c);
+  // Page ids of this split, lane i holding page s + i*nsplit.
   const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
-  const float c2 = a.scale_log2;
+  const int id0 = (lane < n) ? bt[s + lane * nsplit] : 0;
+  const int id1 = (64 + lane < n) ? bt[s + (64 + lane) * nsplit] : 0;
+  auto page_of = [&](int k) -> int32_t {  // k < n
+    return k < 64 ? __builtin_amdgcn_readlane(id0, k) : __builtin_amdgcn_readlane(id1, k - 64);
+  };
 
-  float m[4], lsum[4], acc[4][16];
+  // B operand of S^T = K Q^T: query head 4g + (t % 4), dims 8c..8c+7 and 32+8c..32+8c+7.
+  const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
+  const bf16x8 qb0 = __builtin_bit_cast(bf16x8, ld16(qrow + 8 * c));
+  const bf16x8 qb1 = __builtin_bit_cast(bf16x8, ld16(qrow + 32 + 8 * c));
+
+  // DMA addressing: instruction i loads token rows 8i..8i+7 of the tile; lane
+  // writes LDS bytes 16*lane of its 1 KiB, i.e. row 8i + lane/8, position lane%8,
+  // which holds chunk (lane%8) ^ swz(row).
+  const int tau0 = lane >> 3;
+  const int tau1 = 8 + (lane >> 3);
+  const uint32_t goff0 = (uint32_t)(tau0 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau0)));
+  const uint32_t goff1 = (uint32_t)(tau1 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau1)));
+  auto issue = [&](int slot, int32_t page) {
+    const size_t base = (size_t)(uint32_t)page * (size_t)(kPageTokens * kRowElems);
+    unsigned char* dst = ring[g][slot];
+    __builtin_amdgcn_global_load_lds(a.k_pool + base + goff0, dst, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(a.k_pool + base + goff1, dst + 1024, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(a.v_pool + base + goff0, dst + kTileBytes, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(a.v_pool + base + goff1, dst + kTileBytes + 1024, 16, 0, 2);
+  };
+  // LDS read offsets: K (A operand) token t, chunks c and 4+c; V^T element
+  // (token 4c+q, dim 16nn+t) lives in chunk 2nn + t/8 at element t%8.
+  const int kr0 = t * 128 + 16 * (c ^ swz(t));
+  const int kr1 = t * 128 + 16 * ((4 + c) ^ swz(t));
+  int vr[4][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    lsum[r] = 0.f;
+  for (int nn = 0; nn < 4; ++nn)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[r][i] = 0.f;
-  }
+    for (int q = 0; q < 4; ++q) {
+      const int tau = 4 * c + q;
+      vr[nn][q] = kTileBytes + tau * 128 + 16 * ((2 * nn + (t >> 3)) ^ swz(tau)) + 2 * (t & 7);
+    }
 
-  PageRegs buf[kPrefetch];
+  float m_lane = -INFINITY;  // running maximum (base-2 logits) of head t % 4
+  float l_lane = 0.f;        // sum of this lane's weights (4 tokens per page)
+  f32x4 acc[4];
 #pragma unroll
-  for (int u = 0; u < kPrefetch; ++u)
-    if (p0 + u < p1) load_page(buf[u], a.k_pool, a.v_pool, bt[p0 + u], loff);
+  for (int nn = 0; nn < 4; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int jb = p0; jb < p1; jb += kPrefetch) {
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) {
-      const int j = jb + u;
-      if (j >= p1) break;
-      PageRegs cur = buf[u];
-      if (j + kPrefetch < p1) load_page(buf[u], a.k_pool, a.v_pool, bt[j + kPrefetch], loff);
+  for (int u = 0; u < kRing; ++u)
+    if (u < n) issue(u, page_of(u));
 
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa0, __builtin_bit_cast(bf16x8, cur.k0), s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa1, __builtin_bit_cast(bf16x8, cur.k1), s, 0, 0, 0);
+  for (int kb = 0; kb < n; kb += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int k = kb + u;
+      if (k >= n) break;
+      // this slot's 4 loads have landed: younger loads are those of the next
+      // kRing-1 pages, or none near the end of the split
+      if (k + kRing - 1 < n)
+        wait_vmcnt<4 * (kRing - 1)>();
+      else
+        wait_vmcnt<0>();
+      const unsigned char* tile = ring[g][u];
+      const u32x4 k0 = *reinterpret_cast<const u32x4*>(tile + kr0);
+      const u32x4 k1 = *reinterpret_cast<const u32x4*>(tile + kr1);
+      s16x4 vb[4];
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vb[nn][q] = *reinterpret_cast<const short*>(tile + vr[nn][q]);
+      wait_lgkmcnt0();  // slot fully read: refill it
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + kRing < n) issue(u, page_of(k + kRing));
 
+      const int j = s + k * nsplit;  // logical page index
+      const bool tail = (j + 1) * kPageTokens > L;
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qb0, st, 0, 0, 0);
+      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qb1, st, 0, 0, 0);
       float x[4];
-      const bool tail = (j + 1) * kPageTokens > L;  // wave-uniform
-      const bool valid = !tail || (j * kPageTokens + t) < L;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = valid ? s[r] * c2 : -INFINITY;
-      if (tail && !valid) {
-        cur.v0 = u32x4{0u, 0u, 0u, 0u};
-        cur.v1 = u32x4{0u, 0u, 0u, 0u};
+      for (int r = 0; r < 4; ++r) x[r] = (!tail || j * kPageTokens + 4 * c + r < L) ? st[r] * a.scale_log2 : -INFINITY;
+      if (tail) {  // masked tokens: their V slots may hold anything (NaN included)
+#pragma unroll
+        for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (j * kPageTokens + 4 * c + q >= L) vb[nn][q] = 0;
       }
 
-      bool raise = false;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) raise |= x[r] > m[r];
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+      if (__builtin_amdgcn_ballot_w64(xm > m_lane) != 0) {
+        // page maximum of head t%4 over the 4 row groups, then rescale
+        float pm = fmaxf(xm, __shfl_xor(xm, 16));
+        pm = fmaxf(pm, __shfl_xor(pm, 32));
+        const float mn = fmaxf(m_lane, pm);
+        const float alpha = (mn == m_lane) ? 1.f : __builtin_amdgcn_exp2f(m_lane - mn);
+        m_lane = mn;
+        l_lane *= alpha;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float mn = fmaxf(m[r], row_max16(x[r]));
-          const float alpha = (mn == m[r]) ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
-          m[r] = mn;
-          lsum[r] *= alpha;
+          const float ar = lane_read(alpha, r);  // lane r holds head r
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc[r][i] *= alpha;
+          for (int nn = 0; nn < 4; ++nn) acc[nn][r] *= ar;
         }
       }
-
-      float vf[16];
-      const unsigned vw[8] = {cur.v0[0], cur.v0[1], cur.v0[2], cur.v0[3],
-                              cur.v1[0], cur.v1[1], cur.v1[2], cur.v1[3]};
+      float p[4];
 #pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        vf[2 * w] = bf16_lo(vw[w]);
-        vf[2 * w + 1] = bf16_hi(vw[w]);
-      }
+      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_lane);
+      l_lane += (p[0] + p[1]) + (p[2] + p[3]);
+
+      unsigned hi[4], lo[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __builtin_amdgcn_exp2f(x[r] - m[r]);
-        lsum[r] += p;
+        hi[r] = __builtin_bit_cast(unsigned, p[r]);
+        lo[r] = __builtin_bit_cast(unsigned, p[r] - __builtin_bit_cast(float, hi[r] & 0xffff0000u));
+      }
+      // pack the upper halves (bf16 truncations) of two FP32 values into one dword
+      const s16x4 ahi = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
+                                                        __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)});
+      const s16x4 alo = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
+                                                        __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)});
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[r][i] = fmaf(p, vf[i], acc[r][i]);
+      for (int nn = 0; nn < 4; ++nn) {
+        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nn], acc[nn], 0, 0, 0);
+        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nn], acc[nn], 0, 0, 0);
       }
     }
   }
 
-  // Sum the 16 token lanes of each row; every lane of row c then holds the
-  // totals for the dims of chunk c (rows hold the same l).
+  // l of head r: sum over the 4 row groups; lane r (r < 4) then holds head r.
+  float lt = l_lane + __shfl_xor(l_lane, 16);
+  lt += __shfl_xor(lt, 32);
+  float lr[4], mr[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    lsum[r] = row_sum16(lsum[r]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[r][i] = row_sum16(acc[r][i]);
+    lr[r] = lane_read(lt, r);
+    mr[r] = lane_read(m_lane, r);
   }
-
-  // Lane t of row c stores head h = t / 4, quarter qq = t % 4 of chunk c's 16 dims.
-  const int h = t >> 2, qq = t & 3;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-  float lh = 0.f, mh = 0.f;
+  // every row group holds the same tiles; lane (t, c) stores dim 16c + t of the 4 heads
+  f32x4 o = acc[0];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    if (h == r) {
-      lh = lsum[r];
-      mh = m[r];
+  for (int nn = 1; nn < 4; ++nn)
+    if (c == nn) o = acc[nn];
+  const int d = 16 * c + t;
+  if (nsplit == 1) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (qq == k) o = f32x4{acc[r][4 * k], acc[r][4 * k + 1], acc[r][4 * k + 2], acc[r][4 * k + 3]};
-    }
-  }
-  const float inv = 1.f / lh;
-  o *= inv;
-  // dims of quarter qq of chunk c: qq 0,1 -> 8c + 4qq; qq 2,3 -> 32 + 8c + 4(qq-2)
-  const int d0 = (qq < 2) ? (8 * c + 4 * qq) : (32 + 8 * c + 4 * (qq - 2));
-  const int head = g * kGroup + h;
-  if (npages <= a.part_pages) {
-    float* dst = a.out + ((size_t)b * kQHeads + head) * kHeadDim + d0;
-    *reinterpret_cast<f32x4*>(dst) = o;
+    for (int r = 0; r < 4; ++r) a.out[((size_t)b * kQHeads + g * kGroup + r) * kHeadDim + d] = o[r] / lr[r];
   } else {
-    const size_t row = ((size_t)b * kQHeads + head) * a.S + split;
-    *reinterpret_cast<f32x4*>(a.part_o + row * kHeadDim + d0) = o;
-    if (c == 0 && qq == 0) {
-      a.part_m[row] = mh;
-      a.part_l[row] = lh;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const size_t row = ((size_t)b * kQHeads + g * kGroup + r) * a.S + s;
+      a.part_o[row * kHeadDim + d] = o[r] / lr[r];
+      if (lane == 0) {
+        a.part_m[row] = mr[r];
+        a.part_l[row] = lr[r];
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// merge: one block of 512 threads per sequence; thread = (head, 4 dims).
+// merge: one thread per (sequence, query head, 4 dims).
+//   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s 2^(m_s - max_s m_s)
 
-__global__ __launch_bounds__(512) void merge_kernel(MergeArgs a) {
-  const int b = blockIdx.x;
-  const int head = threadIdx.x >> 4;
-  const int d0 = (threadIdx.x & 15) * 4;
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int b = idx / (kQHeads * 16);
+  if (b >= a.B) return;
+  const int head = (idx >> 4) % kQHeads;
+  const int d0 = (idx & 15) * 4;
+  float* dst = a.out + ((size_t)b * kQHeads + head) * kHeadDim + d0;
   int live = a.S;
   if (a.seq_lens) {
     const int L = a.seq_lens[b];
     if (L <= 0) {
-      if (!a.skip_single)
-        *reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + head) * kHeadDim + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!a.skip_single) *reinterpret_cast<f32x4*>(dst) = f32x4{0.f, 0.f, 0.f, 0.f};
       return;
     }
     live = min(a.S, (L + a.part_tokens - 1) / a.part_tokens);
@@ -281,13 +321,11 @@ __global__ __launch_bounds__(512) void merge_kernel(MergeArgs a) {
       const float l = a.part_l[row + s];
       if (!(l > 0.f)) continue;
       const float w = l * __builtin_amdgcn_exp2f(a.part_m[row + s] - M);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(a.part_o + (row + s) * kHeadDim + d0);
-      num += w * o;
+      num += w * *reinterpret_cast<const f32x4*>(a.part_o + (row + s) * kHeadDim + d0);
       den += w;
     }
   }
-  const f32x4 res = den > 0.f ? num * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
-  *reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + head) * kHeadDim + d0) = res;
+  *reinterpret_cast<f32x4*>(dst) = den > 0.f ? num * (1.f / den) : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // ---------------------------------------------------------------------------
@@ -302,12 +340,13 @@ hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t*
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)B * kKvHeads * a.S), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)B * a.S), dim3(64 * kKvHeads), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(merge_kernel, dim3(B), dim3(kQHeads * 16), 0, stream, a);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
+  const unsigned threads = (unsigned)a.B * kQHeads * 16;
+  hipLaunchKernelGGL(merge_kernel, dim3((threads + 255) / 256), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
