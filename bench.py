@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark: one decode step of paged attention on one MI355X.
 
-A step is, for each of the 16 layers, ``pa_append`` (this step's token of every
-sequence into its page slot) then ``pa_decode`` (batched paged decode attention
-over the shared BF16 page pool), all on one stream, with every input already
-resident in HBM.  The default workload is the full-context batch: 64 sequences
+A step is, for each of the 16 layers, the append of this step's token of every
+sequence into its page slot followed by batched paged decode attention over the
+shared BF16 page pool, issued as one ``pa_append_decode`` call per layer (the
+same work as ``pa_append`` + ``pa_decode``, which is timed too), all on one
+stream, with every input already resident in HBM.  The default workload is the full-context batch: 64 sequences
 at 2048 tokens, 16 layers, 32 query / 8 KV heads, head dim 64, 16-token pages
 (4 GiB of K and V read per step).
 
@@ -152,14 +153,19 @@ def main():
         del src, dst
     torch.cuda.synchronize()
 
-    def step(ev=None):
+    def step(ev=None, separate=False):
         for l in range(lay.n_layers):
             x = inputs[l]
-            ops.pa_append(x["k_new"], x["v_new"], k_pool, v_pool, bt[l], seq_lens)
+            if separate:
+                ops.pa_append(x["k_new"], x["v_new"], k_pool, v_pool, bt[l], seq_lens)
             if ev is not None:
                 ev[l][0].record()
-            ops.pa_decode(x["q"], k_pool, v_pool, bt[l], seq_lens, lay.scale, out=outs[l],
-                          partition_tokens=part, workspace=ws)
+            if separate:
+                ops.pa_decode(x["q"], k_pool, v_pool, bt[l], seq_lens, lay.scale, out=outs[l],
+                              partition_tokens=part, workspace=ws)
+            else:
+                ops.pa_append_decode(x["k_new"], x["v_new"], k_pool, v_pool, x["q"], bt[l], seq_lens, lay.scale,
+                                     out=outs[l], partition_tokens=part, workspace=ws)
             if ev is not None:
                 ev[l][1].record()
 
@@ -176,6 +182,17 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
+
+    # the same step as two calls per layer (pa_append, then pa_decode)
+    for _ in range(args.warmup):
+        step(separate=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step(separate=True)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step_sep = t0.elapsed_time(t1) / args.steps
 
     # decode launches timed one by one (separate pass, same work)
     dec_ms = []
@@ -243,10 +260,11 @@ def main():
         "us_per_step": round(best_ms * 1e3, 2),
         "us_per_step_stream": round(ms_step * 1e3, 2),
         "us_per_step_graph": None if graph_ms is None else round(graph_ms * 1e3, 2),
+        "us_per_step_separate_append_decode": round(ms_step_sep * 1e3, 2),
         "seq_steps_per_s": round(lay.B / (best_ms * 1e-3), 1),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "roofline": {
-            "kernel": "pa_decode (decode kernel + merge when splits exist)",
+            "kernel": "decode_kernel<fused append> (one launch per layer: append, attention, split merge)",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

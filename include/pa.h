@@ -132,10 +132,15 @@ int32_t pa_default_partition_tokens(void);
  *                on the rest of the batch.
  *   workspace    device buffer of at least
  *                pa_decode_workspace_bytes(B, Hq, D, max_blocks, partition_tokens)
- *                bytes (may be NULL when that is 0).  It holds the split
- *                partials (part_o, part_m, part_l in the layout pa_merge takes,
- *                with S = ceil(16*max_blocks / partition_tokens)) and is only
- *                valid until the next call that uses it.
+ *                bytes (may be NULL when that is 0), zero-filled before its
+ *                first use.  It holds the split partials (part_o, part_m,
+ *                part_l in the layout pa_merge takes, with
+ *                S = ceil(16*max_blocks / partition_tokens)) and one int32
+ *                completion counter per sequence; the counters are back at zero
+ *                when the call's work completes, so the buffer can be reused
+ *                without clearing.  Calls that overlap in time must not share
+ *                a workspace.  Splits are combined inside the same kernel by
+ *                the last workgroup of each sequence (no extra launch).
  * Arithmetic: QK^T products of BF16 values are exact in FP32 and summed in
  * FP32; softmax and accumulation are FP32; the exponentials are base 2 with
  * log2(e) folded into the scale.
@@ -145,6 +150,24 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
               float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
               hipStream_t stream);
+
+/*
+ * pa_append_decode - pa_append followed by pa_decode, in one launch.
+ * ([README] KV page pool item and paged decode attention item: the step
+ * appends the new token at its absolute position, then attends over the
+ * sequence's pages including it.)
+ *
+ * Arguments mean what they mean for pa_append and pa_decode; the pools are
+ * written (the row of position L-1 of every sequence with L >= 1, as a bit
+ * copy of k_new / v_new) and out is computed over positions 0..L-1 with that
+ * row.  The pools and out end up bit-identical to pa_append followed by
+ * pa_decode with the same arguments.
+ */
+int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                     uint16_t* v_pool, const uint16_t* q, const int32_t* block_table,
+                     int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
+                     int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_merge - combine split partial states into the attention output.

@@ -25,7 +25,7 @@ struct Plan {
   int32_t part_tokens;
   int32_t part_pages;
   int32_t S;
-  size_t off_m, off_l, bytes;
+  size_t off_m, off_l, off_c, bytes;
 };
 
 // A sequence of length L has ceil(L / part_tokens) splits (each a set of pages),
@@ -40,13 +40,15 @@ int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) 
   p->S = (max_blocks + p->part_pages - 1) / p->part_pages;
   if (p->S <= 1) {
     p->S = 1;
-    p->off_m = p->off_l = p->bytes = 0;
+    p->off_m = p->off_l = p->off_c = p->bytes = 0;
     return PA_OK;
   }
+  // part_o [B][Hq][S][D], part_m [B][Hq][S], part_l [B][Hq][S], counters int32 [B]
   const size_t rows = (size_t)B * pa::kQHeads * p->S;
   p->off_m = round_up(rows * pa::kHeadDim * sizeof(float));
   p->off_l = p->off_m + round_up(rows * sizeof(float));
-  p->bytes = p->off_l + round_up(rows * sizeof(float));
+  p->off_c = p->off_l + round_up(rows * sizeof(float));
+  p->bytes = p->off_c + round_up((size_t)B * sizeof(int32_t));
   return PA_OK;
 }
 
@@ -96,11 +98,17 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_b
   return p.bytes;
 }
 
-int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, float scale,
-              float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
-              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-              hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by pa_decode and pa_append_decode: checks, split plan, one launch.
+int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+               const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, float scale,
+               float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
+               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+               const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool_w, uint16_t* v_pool_w,
+               bool fused_append, hipStream_t stream) {
   if (B < 0 || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT || num_pages <= 0 ||
       num_pages > INT32_MAX || !isfinite(scale))
     return PA_ERR_SHAPE;
@@ -111,8 +119,10 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
   if (pst != PA_OK) return pst;
   if (B == 0) return PA_OK;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return PA_ERR_NULL;
+  if (fused_append && (!k_new || !v_new)) return PA_ERR_NULL;
   if (misaligned(q) || misaligned(k_pool) || misaligned(v_pool) || misaligned(out))
     return PA_ERR_ALIGN;
+  if (fused_append && (misaligned(k_new) || misaligned(v_new))) return PA_ERR_ALIGN;
   // the 1-D grid has B * S workgroups of 512 lanes
   if ((uint64_t)B * plan.S * 512 >= (1ull << 32)) return PA_ERR_SHAPE;
   if (plan.bytes > 0) {
@@ -122,6 +132,10 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
   char* ws = static_cast<char*>(workspace);
   pa::DecodeArgs a;
   a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_pool_w = k_pool_w;
+  a.v_pool_w = v_pool_w;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
   a.block_table = block_table;
@@ -130,25 +144,37 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
   a.part_o = plan.bytes ? reinterpret_cast<float*>(ws) : nullptr;
   a.part_m = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_m) : nullptr;
   a.part_l = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.counters = plan.bytes ? reinterpret_cast<int*>(ws + plan.off_c) : nullptr;
   a.max_blocks = max_blocks;
   a.part_pages = plan.part_pages;
   a.S = plan.S;
   a.scale_log2 = scale * 1.4426950408889634f;
-  if (pa::launch_decode(a, B, stream) != hipSuccess) return PA_ERR_LAUNCH;
-  if (plan.S > 1) {
-    pa::MergeArgs m;
-    m.B = B;
-    m.part_o = a.part_o;
-    m.part_m = a.part_m;
-    m.part_l = a.part_l;
-    m.seq_lens = seq_lens;
-    m.out = out;
-    m.part_tokens = plan.part_tokens;
-    m.S = plan.S;
-    m.skip_single = 1;
-    if (pa::launch_merge(m, stream) != hipSuccess) return PA_ERR_LAUNCH;
-  }
+  if (pa::launch_decode(a, B, fused_append, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+              const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, float scale,
+              float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
+              int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D,
+                    num_pages, partition_tokens, workspace, workspace_bytes, nullptr, nullptr,
+                    nullptr, nullptr, false, stream);
+}
+
+int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                     uint16_t* v_pool, const uint16_t* q, const int32_t* block_table,
+                     int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
+                     int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D,
+                    num_pages, partition_tokens, workspace, workspace_bytes, k_new, v_new, k_pool,
+                    v_pool, true, stream);
 }
 
 int pa_merge(const float* part_o, const float* part_m, const float* part_l,

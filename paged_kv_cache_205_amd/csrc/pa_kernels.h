@@ -17,6 +17,11 @@ constexpr int kRowElems = kKvHeads * kHeadDim;  // bf16 values in one token row 
 
 struct DecodeArgs {
   const uint16_t* q;
+  const uint16_t* k_new;  // fused append only: [B][Hkv][D]
+  const uint16_t* v_new;
+  uint16_t* k_pool_w;     // fused append only: the pools, writable
+  uint16_t* v_pool_w;
+  int* counters;          // [B] split-completion counters, zero between calls
   const uint16_t* k_pool;
   const uint16_t* v_pool;
   const int32_t* block_table;
@@ -46,7 +51,7 @@ struct MergeArgs {
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int B, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int B, bool fused_append, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace pa

@@ -98,6 +98,11 @@ __global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict_
 //   p_lo = bf16 truncation of (p - p_hi); two MFMAs accumulate p_hi V + p_lo V
 //   in FP32, which represents p to about 2^-14 relative.  Result register r of
 //   tile n holds out[head r][16n + t].
+//
+// Splits.  A single-split sequence writes out directly.  Otherwise each split
+// stores its partial state (o = acc / l, m, l per query head) in the workspace,
+// and the sequence's last workgroup to finish (per-sequence atomic counter)
+// merges them: out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).
 
 constexpr int kRing = 2;                                 // LDS slots (pages in flight) per wave
 constexpr int kTileBytes = kPageTokens * kHeadDim * 2;   // one head's K or V rows of a page
@@ -106,8 +111,10 @@ constexpr int kSlotBytes = 2 * kTileBytes;               // K tile then V tile
 // Position permutation of the 16-byte chunks inside LDS token row tau.
 __device__ __forceinline__ int swz(int tau) { return (tau & 7) ^ ((tau >> 3) << 1); }
 
+template <bool kAppend>
 __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char ring[kKvHeads][kRing][kSlotBytes];
+  __shared__ int last_split;
 
   const int s = blockIdx.x % a.S;
   const int b = blockIdx.x / a.S;
@@ -135,6 +142,28 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   auto page_of = [&](int k) -> int32_t {  // k < n
     return k < 64 ? __builtin_amdgcn_readlane(id0, k) : __builtin_amdgcn_readlane(id1, k - 64);
   };
+
+  // Fused append (kAppend): position L-1 lives in page pa = (L-1)/16, owned by
+  // split pa % nsplit at its page index pa / nsplit.  The wave of head g in that
+  // workgroup stores the new K and V rows of head g to the pool (lanes 0-7: K,
+  // 8-15: V, 16 bytes each) and later patches them into its LDS copy of the page,
+  // so the attention sees exactly what pa_append would have written.
+  int k_app = -1;
+  int tau_app = 0;
+  u32x4 new_row = {0u, 0u, 0u, 0u};
+  if (kAppend) {
+    const int pa = (L - 1) / kPageTokens;
+    if (pa % nsplit == s) {
+      k_app = pa / nsplit;
+      tau_app = (L - 1) % kPageTokens;
+      if (lane < 16) {
+        const size_t head_off = ((size_t)b * kKvHeads + g) * kHeadDim + 8 * (lane & 7);
+        new_row = ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
+        const size_t dst = ((size_t)(uint32_t)bt[pa] * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
+        *reinterpret_cast<u32x4*>((lane < 8 ? a.k_pool_w : a.v_pool_w) + dst) = new_row;
+      }
+    }
+  }
 
   // B operand of S^T = K Q^T: query head 4g + (t % 4), dims 8c..8c+7 and 32+8c..32+8c+7.
   const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
@@ -190,7 +219,10 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
         wait_vmcnt<4 * (kRing - 1)>();
       else
         wait_vmcnt<0>();
-      const unsigned char* tile = ring[g][u];
+      unsigned char* tile = ring[g][u];
+      if (kAppend && k == k_app && lane < 16)  // the new token's row, in the swizzled layout
+        *reinterpret_cast<u32x4*>(tile + (lane < 8 ? 0 : kTileBytes) + tau_app * 128 +
+                                  16 * ((lane & 7) ^ swz(tau_app))) = new_row;
       const u32x4 k0 = *reinterpret_cast<const u32x4*>(tile + kr0);
       const u32x4 k1 = *reinterpret_cast<const u32x4*>(tile + kr1);
       s16x4 vb[4];
@@ -276,17 +308,49 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   if (nsplit == 1) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) a.out[((size_t)b * kQHeads + g * kGroup + r) * kHeadDim + d] = o[r] / lr[r];
-  } else {
+    return;
+  }
+  // Partials are written and read with device-scope (sc1) accesses, which are
+  // coherent across the XCDs' L2 caches without whole-cache write-back or
+  // invalidation; each wave waits for its stores to complete before the
+  // workgroup counts itself done.
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const size_t row = ((size_t)b * kQHeads + g * kGroup + r) * a.S + s;
-      a.part_o[row * kHeadDim + d] = o[r] / lr[r];
-      if (lane == 0) {
-        a.part_m[row] = mr[r];
-        a.part_l[row] = lr[r];
-      }
+  for (int r = 0; r < 4; ++r) {
+    const size_t row = ((size_t)b * kQHeads + g * kGroup + r) * a.S + s;
+    __hip_atomic_store(a.part_o + row * kHeadDim + d, o[r] / lr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) {
+      __hip_atomic_store(a.part_m + row, mr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.part_l + row, lr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  wait_vmcnt<0>();
+
+  // The last workgroup of this sequence to finish combines its nsplit partial
+  // states (in split order, so the result does not depend on which one it is)
+  // and resets the sequence's counter for the next call.
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_split = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+  __syncthreads();
+  if (!last_split) return;
+  {
+    const int h = lane >> 4;         // query head 4g + h
+    const int d0 = (lane & 15) * 4;  // dims d0..d0+3
+    const size_t row = ((size_t)b * kQHeads + g * kGroup + h) * a.S;
+    auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    float M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ld(a.part_m + row + sp));
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float w = ld(a.part_l + row + sp) * __builtin_amdgcn_exp2f(ld(a.part_m + row + sp) - M);
+      const float* po = a.part_o + (row + sp) * kHeadDim + d0;
+      num += w * f32x4{ld(po), ld(po + 1), ld(po + 2), ld(po + 3)};
+      den += w;
+    }
+    *reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup + h) * kHeadDim + d0) = num * (1.f / den);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,8 +403,11 @@ hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t*
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int B, hipStream_t stream) {
-  hipLaunchKernelGGL(decode_kernel, dim3((unsigned)B * a.S), dim3(64 * kKvHeads), 0, stream, a);
+hipError_t launch_decode(const DecodeArgs& a, int B, bool fused_append, hipStream_t stream) {
+  if (fused_append)
+    hipLaunchKernelGGL(decode_kernel<true>, dim3((unsigned)B * a.S), dim3(64 * kKvHeads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_kernel<false>, dim3((unsigned)B * a.S), dim3(64 * kKvHeads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -20,7 +20,7 @@ PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN"}
 EXPORTS = ("pa_status_string", "pa_append", "pa_decode_workspace_bytes",
-           "pa_default_partition_tokens", "pa_decode", "pa_merge")
+           "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_merge")
 
 _lib = None
 
@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
     lib.pa_default_partition_tokens.restype = I32
     lib.pa_decode.argtypes = [P, P, P, P, I32, P, F32, P, I32, I32, I32, I32, I64, I32, P, SZ, P]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_append_decode.argtypes = [P, P, P, P, P, P, I32, P, F32, P, I32, I32, I32, I32, I64, I32, P, SZ, P]
+    lib.pa_append_decode.restype = ctypes.c_int
     lib.pa_merge.argtypes = [P, P, P, P, I32, P, I32, I32, I32, I32, P]
     lib.pa_merge.restype = ctypes.c_int
     _lib = lib
@@ -103,8 +105,9 @@ def pa_default_partition_tokens() -> int:
 
 
 def workspace_for(B: int, max_blocks: int, partition_tokens: int = 0, device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled workspace for pa_decode / pa_append_decode (None when none is needed)."""
     n = pa_decode_workspace_bytes(B, max_blocks, partition_tokens)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
 
 def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None,
@@ -125,6 +128,27 @@ def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None,
                        _ptr(out, torch.float32, "out"), B, Hq, Hkv, D, k_pool.shape[0],
                        partition_tokens, ws_ptr, ws_n, _stream(q.device, stream))
     _check("pa_decode", st)
+    return out
+
+
+def pa_append_decode(k_new, v_new, k_pool, v_pool, q, block_table, seq_lens, scale: float, out=None,
+                     partition_tokens: int = 0, workspace=None, stream=None) -> torch.Tensor:
+    """pa_append then pa_decode in one launch; returns out fp32 [B][32][64]."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(B, block_table.shape[1], partition_tokens, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib = load()
+    st = lib.pa_append_decode(_bf16(k_new, "k_new"), _bf16(v_new, "v_new"), _bf16(k_pool, "k_pool"),
+                              _bf16(v_pool, "v_pool"), _bf16(q, "q"), _ptr(block_table, torch.int32, "block_table"),
+                              block_table.shape[1], _ptr(seq_lens, torch.int32, "seq_lens"), float(scale),
+                              _ptr(out, torch.float32, "out"), B, Hq, Hkv, D, k_pool.shape[0],
+                              partition_tokens, ws_ptr, ws_n, _stream(q.device, stream))
+    _check("pa_append_decode", st)
     return out
 
 

@@ -56,10 +56,12 @@ def test_default_partition_and_workspace_sizes(lib):
     # single split: no workspace
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 2048) == 0
     assert lib.pa_decode_workspace_bytes(64, 32, 64, pt // 16, 0) == 0
-    # 8 splits of 256 tokens: part_o + part_m + part_l, each padded to 256 bytes
+    # 8 splits of 256 tokens: part_o + part_m + part_l + one counter per sequence, each padded to 256 bytes
     rows = 64 * 32 * 8
-    want = rows * 64 * 4 + 2 * (((rows * 4) + 255) // 256 * 256)
+    want = rows * 64 * 4 + 2 * (((rows * 4) + 255) // 256 * 256) + 256
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 256) == want
+    # partitions above 2048 tokens act as 2048
+    assert lib.pa_decode_workspace_bytes(4, 32, 64, 256, 4096) == lib.pa_decode_workspace_bytes(4, 32, 64, 256, 2048) > 0
     # invalid sizes report 0
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 24) == 0
     assert lib.pa_decode_workspace_bytes(0, 32, 64, 128, 256) == 0
@@ -120,6 +122,27 @@ def test_decode_validation(lib):
     assert _decode(lib, ws=MIS, ws_bytes=need) == -6
     assert _decode(lib, q=MIS, ws=A, ws_bytes=need) == -6
     assert _decode(lib, B=0) == 0
+
+
+def _append_decode(lib, **kw):
+    args = dict(kn=A, vn=A, k=A, v=A, q=A, bt=A, max_blocks=128, sl=A, scale=0.125, out=A, B=4, Hq=32,
+                Hkv=8, D=64, num_pages=1024, part=256, ws=A, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.pa_append_decode(args["kn"], args["vn"], args["k"], args["v"], args["q"], args["bt"],
+                                args["max_blocks"], args["sl"], args["scale"], args["out"], args["B"],
+                                args["Hq"], args["Hkv"], args["D"], args["num_pages"], args["part"],
+                                args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_append_decode_validation(lib):
+    assert _append_decode(lib, kn=None) == -1
+    assert _append_decode(lib, vn=None) == -1
+    assert _append_decode(lib, q=None) == -1
+    assert _append_decode(lib, kn=MIS) == -6
+    assert _append_decode(lib, part=40) == -2
+    assert _append_decode(lib, D=32) == -3
+    assert _append_decode(lib, ws=None, ws_bytes=0) == -4
+    assert _append_decode(lib, B=0) == 0
 
 
 def _merge(lib, **kw):

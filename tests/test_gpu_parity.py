@@ -271,3 +271,59 @@ def test_merge_standalone_against_oracle_partials():
     check_close(out, ref, "pa_merge with seq_lens")
     out2 = ops.pa_merge(dev(po), dev(pm), dev(pl)).cpu().numpy()  # all splits live; empty ones have l = 0
     check_close(out2, ref, "pa_merge without seq_lens")
+
+
+# ---------------------------------------------------------------- fused append + decode
+
+
+FUSED = [
+    ("small", synth.small),
+    ("fragmented", lambda: synth.fragmented(B=24, n_layers=2)),
+    ("skewed", lambda: synth.skewed(B=48, n_layers=2)),
+    ("full", lambda: synth.full(B=3, n_layers=2)),
+]
+
+
+@pytest.mark.parametrize("partition", [0, 16, 256])
+@pytest.mark.parametrize("name,make", FUSED, ids=[f[0] for f in FUSED])
+def test_append_decode_matches_separate_calls(name, make, partition):
+    """pa_append_decode leaves the pools and out bit-identical to pa_append then pa_decode."""
+    lay = make()
+    d1 = Device(lay)
+    d2 = Device(lay)
+    ws = ops.workspace_for(lay.B, lay.max_blocks, partition)
+    for l in range(min(lay.n_layers, 4)):
+        d1.append(l)
+        o1 = d1.decode(l, partition_tokens=partition)
+        x = d2.inputs[l]
+        o2 = ops.pa_append_decode(x["k_new"], x["v_new"], d2.k_pool, d2.v_pool, x["q"], d2.bt[l], d2.seq_lens,
+                                  lay.scale, partition_tokens=partition, workspace=ws)
+        assert torch.equal(d1.k_pool.view(torch.int16), d2.k_pool.view(torch.int16)), f"layer {l}: K pool"
+        assert torch.equal(d1.v_pool.view(torch.int16), d2.v_pool.view(torch.int16)), f"layer {l}: V pool"
+        assert torch.equal(o1, o2), f"layer {l}: out differs"
+
+
+def test_workspace_reuse_and_counters_reset():
+    """The split counters return to zero: repeated calls on one workspace agree bit for bit."""
+    lay = synth.fragmented(B=16, n_layers=1)
+    d = Device(lay)
+    d.append(0)
+    part = 16
+    ws = ops.workspace_for(lay.B, lay.max_blocks, part)
+    outs = [ops.pa_decode(d.inputs[0]["q"], d.k_pool, d.v_pool, d.bt[0], d.seq_lens, lay.scale,
+                          partition_tokens=part, workspace=ws).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    # workspace layout: part_o, part_m, part_l (each padded to 256 bytes), then int32 counters [B]
+    rnd = lambda x: (x + 255) // 256 * 256
+    rows = lay.B * 32 * (lay.max_blocks * 16 // part)
+    off_c = rnd(rows * 64 * 4) + 2 * rnd(rows * 4)
+    assert ws.numel() == off_c + rnd(lay.B * 4)
+    assert int(ws[off_c:off_c + lay.B * 4].view(torch.int32).abs().sum()) == 0
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+    # other lengths on the same workspace
+    sl2 = torch.clamp(d.seq_lens - 5, min=0)
+    o_small = ops.pa_decode(d.inputs[0]["q"], d.k_pool, d.v_pool, d.bt[0], sl2, lay.scale,
+                            partition_tokens=part, workspace=ws)
+    o_fresh = ops.pa_decode(d.inputs[0]["q"], d.k_pool, d.v_pool, d.bt[0], sl2, lay.scale, partition_tokens=part)
+    assert torch.equal(o_small, o_fresh)
