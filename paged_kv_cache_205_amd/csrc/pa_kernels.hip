@@ -123,6 +123,18 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   const int t = lane & 15;
   const int c = lane >> 4;
 
+  // Block-table entries.  When the table row has at most 128 entries, all of it
+  // is loaded right away (lane i: entries i and 64 + i), overlapping the load of
+  // the sequence length; otherwise the split's own entries are loaded once the
+  // length is known.  Entries past the sequence are loaded but never used.
+  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
+  const bool whole_row = a.max_blocks <= 128;
+  int id0 = 0, id1 = 0;
+  if (whole_row) {
+    id0 = lane < a.max_blocks ? bt[lane] : 0;
+    id1 = 64 + lane < a.max_blocks ? bt[64 + lane] : 0;
+  }
+
   const int L = a.seq_lens[b];
   if (L <= 0) {  // empty sequence: zero its output rows (split 0 only)
     if (s == 0)
@@ -135,12 +147,17 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   if (s >= nsplit) return;
   const int n = (npages - s + nsplit - 1) / nsplit;  // pages s, s + nsplit, ... (n <= part_pages <= 128)
 
-  // Page ids of this split, lane i holding page s + i*nsplit.
-  const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
-  const int id0 = (lane < n) ? bt[s + lane * nsplit] : 0;
-  const int id1 = (64 + lane < n) ? bt[s + (64 + lane) * nsplit] : 0;
+  // The k-th page of this split is entry id_base + k * id_stride of (id0, id1).
+  int id_base = s, id_stride = nsplit;
+  if (!whole_row) {
+    id0 = (lane < n) ? bt[s + lane * nsplit] : 0;
+    id1 = (64 + lane < n) ? bt[s + (64 + lane) * nsplit] : 0;
+    id_base = 0;
+    id_stride = 1;
+  }
   auto page_of = [&](int k) -> int32_t {  // k < n
-    return k < 64 ? __builtin_amdgcn_readlane(id0, k) : __builtin_amdgcn_readlane(id1, k - 64);
+    const int e = id_base + k * id_stride;
+    return e < 64 ? __builtin_amdgcn_readlane(id0, e) : __builtin_amdgcn_readlane(id1, e - 64);
   };
 
   // Fused append (kAppend): position L-1 lives in page pa = (L-1)/16, owned by
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
       if (lane < 16) {
         const size_t head_off = ((size_t)b * kKvHeads + g) * kHeadDim + 8 * (lane & 7);
         new_row = ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
-        const size_t dst = ((size_t)(uint32_t)bt[pa] * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
+        const size_t dst = ((size_t)(uint32_t)page_of(k_app) * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
         *reinterpret_cast<u32x4*>((lane < 8 ? a.k_pool_w : a.v_pool_w) + dst) = new_row;
       }
     }
@@ -338,15 +355,42 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     const int d0 = (lane & 15) * 4;  // dims d0..d0+3
     const size_t row = ((size_t)b * kQHeads + g * kGroup + h) * a.S;
     auto ld = [](const float* p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
+    // Up to 8 splits per round trip; rounds are combined online (for at most 8
+    // splits this is exactly sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m)).
     float M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, ld(a.part_m + row + sp));
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float w = ld(a.part_l + row + sp) * __builtin_amdgcn_exp2f(ld(a.part_m + row + sp) - M);
-      const float* po = a.part_o + (row + sp) * kHeadDim + d0;
-      num += w * f32x4{ld(po), ld(po + 1), ld(po + 2), ld(po + 3)};
-      den += w;
+    for (int c0 = 0; c0 < nsplit; c0 += 8) {
+      float mv[8], lv[8];
+      f32x4 ov[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (c0 + i < nsplit) {
+          const size_t rs = row + c0 + i;
+          const float* po = a.part_o + rs * kHeadDim + d0;
+          mv[i] = ld(a.part_m + rs);
+          lv[i] = ld(a.part_l + rs);
+          ov[i] = f32x4{ld(po), ld(po + 1), ld(po + 2), ld(po + 3)};
+        } else {
+          mv[i] = -INFINITY;
+          lv[i] = 0.f;
+          ov[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float cm = mv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) cm = fmaxf(cm, mv[i]);
+      const float Mn = fmaxf(M, cm);
+      const float carry = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      num *= carry;
+      den *= carry;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float w = lv[i] * __builtin_amdgcn_exp2f(mv[i] - Mn);
+        num += w * ov[i];
+        den += w;
+      }
+      M = Mn;
     }
     *reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup + h) * kHeadDim + d0) = num * (1.f / den);
   }
