@@ -36,6 +36,29 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_full_b64_l2048.md")
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (pa_kernels.hip, pa_api.cpp); else None."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"sha256[^`]*`([0-9a-f]{64})`", text)
+    m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not (m_sha and m_tr):
+        return None
+    h = hashlib.sha256()
+    for f in ("pa_kernels.hip", "pa_api.cpp"):
+        with open(os.path.join(ROOT, "paged_kv_cache_205_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(m_tr.group(1)) if h.hexdigest() == m_sha.group(1) else None
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the FP64 oracle as it stands, on a bounded sample (runs before
 # the GPU is touched so that worker processes fork from a GPU-free parent).
@@ -270,7 +293,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": (measured_traffic() if (lay.name == "full" and args.partition == 0) else None),
             "bytes_per_launch": lay.kv_bytes_per_layer,
             "mean_launch_us": round(dec_ms_mean * 1e3, 3),
         },

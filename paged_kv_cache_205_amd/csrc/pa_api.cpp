@@ -8,7 +8,7 @@
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 512;
+constexpr int32_t kDefaultPartitionTokens = 768;
 constexpr int32_t kMaxPartitionTokens = 2048;  // a split holds at most 128 pages
 constexpr size_t kAlign = 256;
 

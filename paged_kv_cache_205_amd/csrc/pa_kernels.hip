@@ -104,7 +104,10 @@ __global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict_
 // and the sequence's last workgroup to finish (per-sequence atomic counter)
 // merges them: out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).
 
-constexpr int kRing = 2;                                 // LDS slots (pages in flight) per wave
+#ifndef PA_RING_PAGES
+#define PA_RING_PAGES 2
+#endif
+constexpr int kRing = PA_RING_PAGES;                     // LDS slots (pages in flight) per wave
 constexpr int kTileBytes = kPageTokens * kHeadDim * 2;   // one head's K or V rows of a page
 constexpr int kSlotBytes = 2 * kTileBytes;               // K tile then V tile
 
