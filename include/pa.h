@@ -64,6 +64,7 @@ extern "C" {
 #define PA_KV_HEADS 8
 #define PA_Q_HEADS 32
 #define PA_MAX_BLOCKS_LIMIT 4096
+#define PA_MAX_DECODE_BATCH 4096
 
 enum pa_status {
   PA_OK = 0,
@@ -99,14 +100,14 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
               int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
 
 /*
- * Bytes of workspace pa_decode needs for these sizes (0 when no sequence can
- * have more than one split).  partition_tokens = 0 selects the default.
- * Returns 0 for invalid sizes as well; pa_decode reports those.
+ * Bytes of workspace pa_decode and pa_append_decode need for these sizes
+ * (partition_tokens = 0: automatic split size).  Returns 0 for invalid sizes;
+ * the calls report those.
  */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
                                  int32_t partition_tokens);
 
-/* The partition (tokens per split) pa_decode uses when passed 0. */
+/* The partition_tokens value that selects the automatic split size (0). */
 int32_t pa_default_partition_tokens(void);
 
 /*
@@ -121,26 +122,29 @@ int32_t pa_default_partition_tokens(void);
  *   q            bf16 [B][Hq][D] (already position-encoded)
  *   out          fp32 [B][Hq][D]; rows of sequences with L == 0 are set to 0
  *   scale        softmax scale (1/sqrt(D) for the model)
- *   partition_tokens  split size in tokens, a multiple of 16 (0 = default,
- *                pa_default_partition_tokens(); values above 2048 act as 2048).
- *                A sequence of L tokens (npages = ceil(L/16) pages) is processed
- *                as S_b = ceil(L / partition_tokens) splits; split s takes the
- *                pages s, s + S_b, s + 2 S_b, ...  When S_b > 1 the partial
- *                states are combined by the merge kernel (the same kernel as
- *                pa_merge) in the same call.  The splits of a sequence depend
- *                only on its own length, so a sequence's output does not depend
- *                on the rest of the batch.
+ *   partition_tokens  split size in tokens, a multiple of 16; values above
+ *                2048 act as 2048.  A sequence of L tokens (npages = ceil(L/16)
+ *                pages) is processed as S_b = ceil(npages / pp) splits with
+ *                pp = partition_tokens / 16 pages; split s takes the pages
+ *                s, s + S_b, s + 2 S_b, ...  With partition_tokens > 0 the splits
+ *                of a sequence depend only on its own length, so its output is
+ *                bit-identical whatever else is in the batch.  With 0
+ *                (automatic) pp = clamp(ceil(total pages of the batch / 192), 8,
+ *                128): large batches get few, long splits and small or skewed
+ *                batches get more; results then may differ in rounding between
+ *                batches.  When S_b > 1 the splits' partial states are merged
+ *                inside the same launch.
+ *   B            at most PA_MAX_DECODE_BATCH (the work plan lives in LDS).
  *   workspace    device buffer of at least
  *                pa_decode_workspace_bytes(B, Hq, D, max_blocks, partition_tokens)
- *                bytes (may be NULL when that is 0), zero-filled before its
- *                first use.  It holds the split partials (part_o, part_m,
- *                part_l in the layout pa_merge takes, with
- *                S = ceil(16*max_blocks / partition_tokens)) and one int32
- *                completion counter per sequence; the counters are back at zero
- *                when the call's work completes, so the buffer can be reused
- *                without clearing.  Calls that overlap in time must not share
- *                a workspace.  Splits are combined inside the same kernel by
- *                the last workgroup of each sequence (no extra launch).
+ *                bytes, zero-filled before its first use.  It holds the split
+ *                partials (part_o, part_m, part_l in the layout pa_merge takes,
+ *                with S = ceil(max_blocks / smallest split in pages)), one int32
+ *                completion counter per sequence and a work-queue counter; the
+ *                counters are back at zero when the call's work completes, so
+ *                the buffer can be reused without clearing.  Calls that overlap
+ *                in time must not share a workspace.  Splits are combined inside
+ *                the same kernel by the last workgroup of each sequence.
  * Arithmetic: QK^T products of BF16 values are exact in FP32 and summed in
  * FP32; softmax and accumulation are FP32; the exponentials are base 2 with
  * log2(e) folded into the scale.

@@ -8,8 +8,9 @@
 
 namespace {
 
-constexpr int32_t kDefaultPartitionTokens = 768;
 constexpr int32_t kMaxPartitionTokens = 2048;  // a split holds at most 128 pages
+constexpr int32_t kAutoMinPages = 8;           // smallest split the automatic choice makes
+constexpr int32_t kTargetItems = 192;          // automatic choice: about this many large items per call
 constexpr size_t kAlign = 256;
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -22,34 +23,62 @@ int check_dims(int32_t Hq, int32_t Hkv, int32_t D) {
 }
 
 struct Plan {
-  int32_t part_tokens;
-  int32_t part_pages;
-  int32_t S;
-  size_t off_m, off_l, off_c, bytes;
+  int32_t part_pages;  // 0: automatic (decided on the device from the batch)
+  int32_t S;           // upper bound of any sequence's split count = partial rows per (b, h)
+  size_t off_m, off_l, off_c, off_q, bytes;
 };
 
-// A sequence of length L has ceil(L / part_tokens) splits (each a set of pages),
-// independent of the rest of the batch.
+// With partition_tokens > 0 a sequence of L tokens has ceil(L / partition_tokens)
+// splits, independent of the rest of the batch.  With 0 the kernel picks the
+// split size from the batch's total pages (at least 8 pages per split).
 int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) {
   if (partition_tokens < 0 || partition_tokens % pa::kPageTokens != 0) return PA_ERR_SHAPE;
-  int32_t pt = partition_tokens == 0 ? kDefaultPartitionTokens : partition_tokens;
-  if (pt > kMaxPartitionTokens) pt = kMaxPartitionTokens;
-  p->part_pages = pt / pa::kPageTokens;
-  if (p->part_pages >= max_blocks) p->part_pages = max_blocks;
-  p->part_tokens = p->part_pages * pa::kPageTokens;
-  p->S = (max_blocks + p->part_pages - 1) / p->part_pages;
-  if (p->S <= 1) {
-    p->S = 1;
-    p->off_m = p->off_l = p->off_c = p->bytes = 0;
-    return PA_OK;
+  int32_t min_pages;
+  if (partition_tokens == 0) {
+    p->part_pages = 0;
+    min_pages = kAutoMinPages;
+  } else {
+    const int32_t pt = partition_tokens > kMaxPartitionTokens ? kMaxPartitionTokens : partition_tokens;
+    p->part_pages = pt / pa::kPageTokens;
+    min_pages = p->part_pages;
   }
-  // part_o [B][Hq][S][D], part_m [B][Hq][S], part_l [B][Hq][S], counters int32 [B]
-  const size_t rows = (size_t)B * pa::kQHeads * p->S;
+  p->S = (max_blocks + min_pages - 1) / min_pages;
+  if (p->S < 1) p->S = 1;
+  // part_o [B][Hq][S][D], part_m [B][Hq][S], part_l [B][Hq][S] (only when a
+  // sequence can have several splits), counters int32 [B], queue int32 [2]
+  const size_t rows = p->S > 1 ? (size_t)B * pa::kQHeads * p->S : 0;
   p->off_m = round_up(rows * pa::kHeadDim * sizeof(float));
   p->off_l = p->off_m + round_up(rows * sizeof(float));
   p->off_c = p->off_l + round_up(rows * sizeof(float));
-  p->bytes = p->off_c + round_up((size_t)B * sizeof(int32_t));
+  p->off_q = p->off_c + round_up((size_t)B * sizeof(int32_t));
+  p->bytes = p->off_q + kAlign;
   return PA_OK;
+}
+
+// Workgroups the decode grid gets: an upper bound of the number of work items,
+// capped at what the GPU holds at once (2 workgroups per CU while the plan's
+// LDS fits beside the page ring, else 1).  *bounded is set when the bound fits,
+// i.e. every item has a workgroup of its own.
+int decode_grid(int32_t B, int32_t max_blocks, const Plan& p, bool* bounded) {
+  uint64_t items;
+  if (p.part_pages > 0) {
+    items = (uint64_t)B * p.S;
+  } else {
+    // sum_b ceil(np_b / pp) < B + total/pp, and total/pp is at most kTargetItems
+    // unless pp is capped at 128 pages, when it is at most ceil(B * max_blocks / 128)
+    const uint64_t capped = ((uint64_t)B * (uint64_t)max_blocks + 127) / 128;
+    const uint64_t bound = (uint64_t)B + (capped > (uint64_t)kTargetItems ? capped : (uint64_t)kTargetItems);
+    const uint64_t all = (uint64_t)B * p.S;
+    items = bound < all ? bound : all;
+  }
+  int cus = 256, dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    cus = n;
+  const int per_cu = pa::decode_lds_bytes(B) <= 80 * 1024 ? 2 : 1;
+  const uint64_t cap = (uint64_t)cus * per_cu;
+  *bounded = items <= cap;
+  return (int)(items < cap ? items : cap);
 }
 
 }  // namespace
@@ -69,7 +98,7 @@ const char* pa_status_string(int status) {
   }
 }
 
-int32_t pa_default_partition_tokens(void) { return kDefaultPartitionTokens; }
+int32_t pa_default_partition_tokens(void) { return 0; }
 
 int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
               const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
@@ -91,7 +120,7 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
 
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
                                  int32_t partition_tokens) {
-  if (B <= 0 || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return 0;
+  if (B <= 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return 0;
   if (check_dims(Hq, pa::kKvHeads, D) != PA_OK) return 0;
   Plan p;
   if (make_plan(B, max_blocks, partition_tokens, &p) != PA_OK) return 0;
@@ -109,8 +138,8 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
                int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool_w, uint16_t* v_pool_w,
                bool fused_append, hipStream_t stream) {
-  if (B < 0 || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT || num_pages <= 0 ||
-      num_pages > INT32_MAX || !isfinite(scale))
+  if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT ||
+      num_pages <= 0 || num_pages > INT32_MAX || !isfinite(scale))
     return PA_ERR_SHAPE;
   const int dims = check_dims(Hq, Hkv, D);
   if (dims != PA_OK) return dims;
@@ -123,12 +152,8 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   if (misaligned(q) || misaligned(k_pool) || misaligned(v_pool) || misaligned(out))
     return PA_ERR_ALIGN;
   if (fused_append && (misaligned(k_new) || misaligned(v_new))) return PA_ERR_ALIGN;
-  // the 1-D grid has B * S workgroups of 512 lanes
-  if ((uint64_t)B * plan.S * 512 >= (1ull << 32)) return PA_ERR_SHAPE;
-  if (plan.bytes > 0) {
-    if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
-    if (misaligned(workspace)) return PA_ERR_ALIGN;
-  }
+  if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return PA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
   pa::DecodeArgs a;
   a.q = q;
@@ -141,15 +166,23 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.block_table = block_table;
   a.seq_lens = seq_lens;
   a.out = out;
-  a.part_o = plan.bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_m = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_m) : nullptr;
-  a.part_l = plan.bytes ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
-  a.counters = plan.bytes ? reinterpret_cast<int*>(ws + plan.off_c) : nullptr;
+  a.part_o = plan.S > 1 ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_m = plan.S > 1 ? reinterpret_cast<float*>(ws + plan.off_m) : nullptr;
+  a.part_l = plan.S > 1 ? reinterpret_cast<float*>(ws + plan.off_l) : nullptr;
+  a.counters = reinterpret_cast<int*>(ws + plan.off_c);
+  a.B = B;
   a.max_blocks = max_blocks;
   a.part_pages = plan.part_pages;
   a.S = plan.S;
   a.scale_log2 = scale * 1.4426950408889634f;
-  if (pa::launch_decode(a, B, fused_append, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  // the plan when every sequence fills its table row
+  a.guess_pp = plan.part_pages > 0 ? plan.part_pages : pa::auto_split_pages((long long)B * max_blocks);
+  a.guess_ns = (max_blocks + a.guess_pp - 1) / a.guess_pp;
+  a.guess_magic = a.guess_ns > 1 ? (uint32_t)(((1ull << 32) + a.guess_ns - 1) / a.guess_ns) : 0u;
+  bool bounded = false;
+  const int grid = decode_grid(B, max_blocks, plan, &bounded);
+  a.queue = bounded ? nullptr : reinterpret_cast<int*>(ws + plan.off_q);
+  if (pa::launch_decode(a, grid, fused_append, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

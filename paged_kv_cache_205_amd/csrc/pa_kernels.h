@@ -14,26 +14,36 @@ constexpr int kKvHeads = 8;
 constexpr int kQHeads = 32;
 constexpr int kGroup = kQHeads / kKvHeads;
 constexpr int kRowElems = kKvHeads * kHeadDim;  // bf16 values in one token row of a page plane
+constexpr int kMaxDecodeBatch = 4096;           // the work plan keeps 3 ints per sequence in LDS
 
 struct DecodeArgs {
+  // the fields read at the start of the kernel fill the first 64 bytes
+  const int32_t* seq_lens;
+  const int32_t* block_table;
   const uint16_t* q;
   const uint16_t* k_new;  // fused append only: [B][Hkv][D]
   const uint16_t* v_new;
-  uint16_t* k_pool_w;     // fused append only: the pools, writable
-  uint16_t* v_pool_w;
-  int* counters;          // [B] split-completion counters, zero between calls
+  int B;
+  int max_blocks;
+  // The split plan of a batch in which every sequence fills its table row
+  // (computed on the host from the sizes alone): splits per sequence,
+  // ceil(2^32 / guess_ns) for dividing by it (guess_ns > 1), pages per split.
+  int guess_ns;
+  uint32_t guess_magic;
+  int guess_pp;
+  int part_pages;  // pages per split (<= 128); 0: chosen per call from the batch's total pages
   const uint16_t* k_pool;
   const uint16_t* v_pool;
-  const int32_t* block_table;
-  const int32_t* seq_lens;
+  int S;             // row stride of the partials: an upper bound of any sequence's split count
+  float scale_log2;  // scale * log2(e)
+  uint16_t* k_pool_w;  // fused append only: the pools, writable
+  uint16_t* v_pool_w;
+  int* counters;  // [B] split-completion counters, zero between calls
+  int* queue;     // {next item, workgroups done}, zero between calls; NULL: one item per workgroup
   float* out;
   float* part_o;  // [B][Hq][S][D]
   float* part_m;  // [B][Hq][S]
   float* part_l;  // [B][Hq][S]
-  int max_blocks;
-  int part_pages;    // a sequence of npages pages has ceil(npages / part_pages) splits (part_pages <= 128)
-  int S;             // splits per sequence in the grid = ceil(max_blocks / part_pages)
-  float scale_log2;  // scale * log2(e)
 };
 
 struct MergeArgs {
@@ -51,7 +61,10 @@ struct MergeArgs {
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);
-hipError_t launch_decode(const DecodeArgs& a, int B, bool fused_append, hipStream_t stream);
+size_t decode_lds_bytes(int B);
+// Pages per split that the automatic plan picks for a batch with this many pages.
+int auto_split_pages(long long total_pages);
+hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace pa

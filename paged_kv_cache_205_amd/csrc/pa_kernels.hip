@@ -114,41 +114,71 @@ constexpr int kSlotBytes = 2 * kTileBytes;               // K tile then V tile
 // Position permutation of the 16-byte chunks inside LDS token row tau.
 __device__ __forceinline__ int swz(int tau) { return (tau & 7) ^ ((tau >> 3) << 1); }
 
-template <bool kAppend>
-__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char ring[kKvHeads][kRing][kSlotBytes];
-  __shared__ int last_split;
+// One work item: split s (of nsplit) of sequence b, whose length is L.  Called
+// by all 8 waves of the workgroup with the same arguments.
+// DMA addressing of one page tile: instruction i loads token rows 8i..8i+7;
+// lane writes LDS bytes 16*lane of its 1 KiB, i.e. row 8i + lane/8, position
+// lane%8, which holds chunk (lane%8) ^ swz(row).
+struct DmaOffsets {
+  uint32_t off0, off1;  // element offsets within a page for rows lane/8 and 8 + lane/8
+};
+__device__ __forceinline__ DmaOffsets dma_offsets(int lane, int g) {
+  const int tau0 = lane >> 3;
+  const int tau1 = 8 + (lane >> 3);
+  return DmaOffsets{(uint32_t)(tau0 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau0))),
+                    (uint32_t)(tau1 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau1)))};
+}
+// Starts the copy of head g's K and V tiles of one page into an LDS slot.
+__device__ __forceinline__ void issue_page(const DecodeArgs& a, unsigned char* dst, int32_t page, DmaOffsets o) {
+  const size_t base = (size_t)(uint32_t)page * (size_t)(kPageTokens * kRowElems);
+  const uint16_t* kp = a.k_pool + base;
+  const uint16_t* vp = a.v_pool + base;
+  __builtin_amdgcn_global_load_lds(kp + o.off0, dst, 16, 0, 2);
+  __builtin_amdgcn_global_load_lds(kp + o.off1, dst + 1024, 16, 0, 2);
+  __builtin_amdgcn_global_load_lds(vp + o.off0, dst + kTileBytes, 16, 0, 2);
+  __builtin_amdgcn_global_load_lds(vp + o.off1, dst + kTileBytes + 1024, 16, 0, 2);
+}
 
-  const int s = blockIdx.x % a.S;
-  const int b = blockIdx.x / a.S;
+// Table row and q of one sequence, loaded ahead of its item (b < 0: none).
+struct ItemPrefetch {
+  int b;
+  int id0, id1;
+  u32x4 q0, q1;
+  u32x4 row;  // appended K (lanes 0-7) / V (lanes 8-15) row of the wave's head
+};
+
+template <bool kAppend>
+__device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, int nsplit, int L, int n,
+                                            const ItemPrefetch& pre, bool primed, DmaOffsets doff,
+                                            unsigned char (*ring)[kRing][kSlotBytes], int* last_split) {
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  // lane index produced anew for every item, so that nothing derived from it is
+  // hoisted out of the item loop and kept live across items
+  int lane;
+  asm volatile("v_and_b32 %0, 63, %1" : "=v"(lane) : "v"(threadIdx.x));
   const int t = lane & 15;
   const int c = lane >> 4;
 
-  // Block-table entries.  When the table row has at most 128 entries, all of it
-  // is loaded right away (lane i: entries i and 64 + i), overlapping the load of
-  // the sequence length; otherwise the split's own entries are loaded once the
-  // length is known.  Entries past the sequence are loaded but never used.
+  if (L <= 0) {  // empty sequence: zero its output rows
+    reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup) * kHeadDim)[lane] =
+        f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+
+  // Block-table entries.  When the table row has at most 128 entries all of it
+  // is loaded (lane i: entries i and 64 + i); otherwise the split's own entries.
+  // Entries past the sequence are loaded but never used.
   const int32_t* bt = a.block_table + (size_t)b * a.max_blocks;
   const bool whole_row = a.max_blocks <= 128;
+  const bool prefetched = whole_row && pre.b == b;
   int id0 = 0, id1 = 0;
-  if (whole_row) {
+  if (prefetched) {
+    id0 = pre.id0;
+    id1 = pre.id1;
+  } else if (whole_row) {
     id0 = lane < a.max_blocks ? bt[lane] : 0;
     id1 = 64 + lane < a.max_blocks ? bt[64 + lane] : 0;
   }
-
-  const int L = a.seq_lens[b];
-  if (L <= 0) {  // empty sequence: zero its output rows (split 0 only)
-    if (s == 0)
-      reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup) * kHeadDim)[lane] =
-          f32x4{0.f, 0.f, 0.f, 0.f};
-    return;
-  }
-  const int npages = (L + kPageTokens - 1) / kPageTokens;
-  const int nsplit = (npages + a.part_pages - 1) / a.part_pages;
-  if (s >= nsplit) return;
-  const int n = (npages - s + nsplit - 1) / nsplit;  // pages s, s + nsplit, ... (n <= part_pages <= 128)
 
   // The k-th page of this split is entry id_base + k * id_stride of (id0, id1).
   int id_base = s, id_stride = nsplit;
@@ -178,7 +208,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
       tau_app = (L - 1) % kPageTokens;
       if (lane < 16) {
         const size_t head_off = ((size_t)b * kKvHeads + g) * kHeadDim + 8 * (lane & 7);
-        new_row = ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
+        new_row = prefetched ? pre.row : ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
         const size_t dst = ((size_t)(uint32_t)page_of(k_app) * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
         *reinterpret_cast<u32x4*>((lane < 8 ? a.k_pool_w : a.v_pool_w) + dst) = new_row;
       }
@@ -187,24 +217,10 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 
   // B operand of S^T = K Q^T: query head 4g + (t % 4), dims 8c..8c+7 and 32+8c..32+8c+7.
   const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
-  const bf16x8 qb0 = __builtin_bit_cast(bf16x8, ld16(qrow + 8 * c));
-  const bf16x8 qb1 = __builtin_bit_cast(bf16x8, ld16(qrow + 32 + 8 * c));
+  const bf16x8 qb0 = __builtin_bit_cast(bf16x8, prefetched ? pre.q0 : ld16(qrow + 8 * c));
+  const bf16x8 qb1 = __builtin_bit_cast(bf16x8, prefetched ? pre.q1 : ld16(qrow + 32 + 8 * c));
 
-  // DMA addressing: instruction i loads token rows 8i..8i+7 of the tile; lane
-  // writes LDS bytes 16*lane of its 1 KiB, i.e. row 8i + lane/8, position lane%8,
-  // which holds chunk (lane%8) ^ swz(row).
-  const int tau0 = lane >> 3;
-  const int tau1 = 8 + (lane >> 3);
-  const uint32_t goff0 = (uint32_t)(tau0 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau0)));
-  const uint32_t goff1 = (uint32_t)(tau1 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau1)));
-  auto issue = [&](int slot, int32_t page) {
-    const size_t base = (size_t)(uint32_t)page * (size_t)(kPageTokens * kRowElems);
-    unsigned char* dst = ring[g][slot];
-    __builtin_amdgcn_global_load_lds(a.k_pool + base + goff0, dst, 16, 0, 2);
-    __builtin_amdgcn_global_load_lds(a.k_pool + base + goff1, dst + 1024, 16, 0, 2);
-    __builtin_amdgcn_global_load_lds(a.v_pool + base + goff0, dst + kTileBytes, 16, 0, 2);
-    __builtin_amdgcn_global_load_lds(a.v_pool + base + goff1, dst + kTileBytes + 1024, 16, 0, 2);
-  };
+  auto issue = [&](int slot, int32_t page) { issue_page(a, ring[g][slot], page, doff); };
   // LDS read offsets: K (A operand) token t, chunks c and 4+c; V^T element
   // (token 4c+q, dim 16nn+t) lives in chunk 2nn + t/8 at element t%8.
   const int kr0 = t * 128 + 16 * (c ^ swz(t));
@@ -224,9 +240,11 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nn = 0; nn < 4; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  if (!primed) {
 #pragma unroll
-  for (int u = 0; u < kRing; ++u)
-    if (u < n) issue(u, page_of(u));
+    for (int u = 0; u < kRing; ++u)
+      if (u < n) issue(u, page_of(u));
+  }
 
   for (int kb = 0; kb < n; kb += kRing) {
 #pragma unroll
@@ -350,9 +368,9 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   // and resets the sequence's counter for the next call.
   __syncthreads();
   if (threadIdx.x == 0)
-    last_split = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
+    *last_split = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
   __syncthreads();
-  if (!last_split) return;
+  if (!*last_split) return;
   {
     const int h = lane >> 4;         // query head 4g + h
     const int d0 = (lane & 15) * 4;  // dims d0..d0+3
@@ -398,6 +416,356 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     *reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup + h) * kHeadDim + d0) = num * (1.f / den);
   }
   if (threadIdx.x == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+
+// ---------------------------------------------------------------------------
+// Work plan.  Every workgroup builds the same plan in LDS from seq_lens:
+//   pp      pages per split: a.part_pages if set, else ceil(total pages / 192)
+//           clamped to [8, 128] (so a batch yields about 192 large items);
+//   nsplit  ceil(npages / pp) splits per sequence (1 for an empty sequence);
+//   items   first every split of the multi-split sequences (sequence-major),
+//           then the single-split sequences.  Workgroup w starts with item w;
+//           if there are more items than workgroups the rest are handed out
+//           by an atomic queue.  Long sequences' splits, the largest items,
+//           start first, and no workgroup is launched without work.
+
+constexpr int kTargetItems = 192;
+constexpr int kAutoMinPages = 8;
+constexpr int kMaxSplitPages = 128;
+
+__host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages) {
+  return min(kMaxSplitPages, max(kAutoMinPages, (total_pages + kTargetItems - 1) / kTargetItems));
+}
+
+__device__ __forceinline__ int nsplit_of(int L, int pp) {
+  if (L <= 0) return 1;
+  const int np = (L + kPageTokens - 1) / kPageTokens;
+  return (np + pp - 1) / pp;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within rows of 16
+// lanes through DPP, then the row totals added through readlane.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// Maximum over the 64 lanes of a wave of values >= 0 (same pattern as the scan).
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false));
+  return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+             max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+}
+
+// Largest b with pre[b] <= i, for a nondecreasing pre[0..B] with pre[0] = 0 <= i < pre[B].
+__device__ __forceinline__ int owner_of(const int* pre, int B, int i) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= i) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// The work plan, shared by the workgroup through LDS.
+struct PlanLds {
+  int wave_pages[8];   // pages per wave
+  int wave_max[8];     // largest page count per wave
+  int wave_min[8];     // kPageCap minus the smallest page count per wave
+  int wave_multi[8];   // multi-split items per wave
+  int wave_single[8];  // single-split items per wave
+  int first[2];        // (sequence, split) of item blockIdx.x
+  int pp;              // pages per split
+  int uniform_ns;      // as in ItemPlan
+};
+struct ItemPlan {
+  int pp, n_multi, n_items;
+  int uniform_ns;     // > 0: every sequence has this many splits, item i is (i / ns, i % ns)
+  int uniform_pages;  // with uniform_ns > 0: every sequence's page count
+};
+constexpr int kPageCap = 1 << 20;  // above any page count of a sequence
+
+// Workgroup barrier for LDS data: waits for this wave's LDS accesses, not for
+// its outstanding global loads or copies into LDS.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The plan is built in two steps so that the caller can start work between
+// them: plan_lengths loads the lengths (thread t handles sequences
+// [t*per, t*per + per)) into sL and sums their pages; plan_finish derives the
+// items in LDS (sA / sC: exclusive prefixes of the multi-split and single-split
+// item counts, pl->first: this workgroup's first item).  When every sequence
+// has the same number of pages the items follow from the index alone and the
+// plan ends after its first barrier.
+struct PlanLengths {
+  int pages, pmax, pmin_c;  // this thread's page sum, largest count, kPageCap - smallest count
+};
+__device__ __forceinline__ PlanLengths plan_lengths(const int32_t* __restrict__ seq_lens, int B, int len0, int* sL) {
+  const int per = (B + 511) / 512;
+  const int b0 = min(B, (int)threadIdx.x * per), b1 = min(B, b0 + per);
+  PlanLengths x{0, 0, 0};
+  for (int b = b0; b < b1; ++b) {
+    const int L = b == b0 ? len0 : seq_lens[b];
+    sL[b] = L;
+    const int np = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
+    x.pages += np;
+    x.pmax = max(x.pmax, np);
+    x.pmin_c = max(x.pmin_c, kPageCap - np);
+  }
+  return x;
+}
+
+__device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_pages, int* sL, int* sA, int* sC,
+                                                PlanLds* pl) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int per = (B + 511) / 512;
+  const int b0 = min(B, (int)threadIdx.x * per), b1 = min(B, b0 + per);
+  const int tp = wave_inclusive_scan(x.pages);
+  const int pmax = wave_max_nonneg(x.pmax);
+  const int pmin_c = wave_max_nonneg(x.pmin_c);
+  if (lane == 63) {
+    pl->wave_pages[w] = tp;
+    pl->wave_max[w] = pmax;
+    pl->wave_min[w] = pmin_c;
+  }
+  lds_barrier();
+  int total_pages = 0, all_max = 0, all_min_c = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    total_pages += pl->wave_pages[v];
+    all_max = max(all_max, pl->wave_max[v]);
+    all_min_c = max(all_min_c, pl->wave_min[v]);
+  }
+  const int pp = part_pages > 0 ? part_pages : auto_pages_per_split(total_pages);
+  ItemPlan p;
+  p.pp = pp;
+  if (kPageCap - all_min_c == all_max) {  // uniform page count
+    const int ns = all_max > 0 ? (all_max + pp - 1) / pp : 1;
+    p.uniform_ns = ns;
+    p.uniform_pages = all_max;
+    p.n_items = B * ns;
+    p.n_multi = ns > 1 ? p.n_items : 0;
+    if (threadIdx.x == 0) {  // read back only after later barriers
+      pl->pp = pp;
+      pl->uniform_ns = ns;
+      sA[B] = p.n_multi;
+      sC[B] = p.n_items - p.n_multi;
+    }
+    return p;
+  }
+  int ca = 0, cc = 0;
+  for (int b = b0; b < b1; ++b) {  // sL[b] was written by this thread
+    const int ns = nsplit_of(sL[b], pp);
+    ca += ns > 1 ? ns : 0;
+    cc += ns > 1 ? 0 : 1;
+  }
+  const int ia = wave_inclusive_scan(ca), ic = wave_inclusive_scan(cc);
+  if (lane == 63) {
+    pl->wave_multi[w] = ia;
+    pl->wave_single[w] = ic;
+  }
+  lds_barrier();
+  int oa = ia - ca, oc = ic - cc, n_multi = 0, n_single = 0;
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int xa = pl->wave_multi[v], xc = pl->wave_single[v];
+    oa += v < w ? xa : 0;
+    oc += v < w ? xc : 0;
+    n_multi += xa;
+    n_single += xc;
+  }
+  const int i0 = blockIdx.x;
+  for (int b = b0; b < b1; ++b) {
+    const int ns = nsplit_of(sL[b], pp);
+    sA[b] = oa;
+    sC[b] = oc;
+    if (ns > 1 && i0 >= oa && i0 < oa + ns) {
+      pl->first[0] = b;
+      pl->first[1] = i0 - oa;
+    }
+    if (ns == 1 && i0 == n_multi + oc) {
+      pl->first[0] = b;
+      pl->first[1] = 0;
+    }
+    oa += ns > 1 ? ns : 0;
+    oc += ns > 1 ? 0 : 1;
+  }
+  if (threadIdx.x == 0) {
+    sA[B] = n_multi;
+    sC[B] = n_single;
+    pl->pp = pp;
+    pl->uniform_ns = 0;
+  }
+  lds_barrier();
+  p.uniform_ns = 0;
+  p.uniform_pages = 0;
+  p.n_multi = n_multi;
+  p.n_items = n_multi + n_single;
+  return p;
+}
+
+template <bool kAppend>
+__global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
+  // Dynamic LDS: the page ring, then the plan's per-sequence arrays.
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto ring = reinterpret_cast<unsigned char (*)[kRing][kSlotBytes]>(smem);
+  int* plan_arrays = reinterpret_cast<int*>(smem + kKvHeads * kRing * kSlotBytes);
+  __shared__ PlanLds plan_lds;
+  __shared__ int last_split;
+  __shared__ int next_item;
+  const int B = a.B;
+  int* sL = plan_arrays;  // [B] lengths
+  int* sA = sL + B;       // [B+1] multi-split item prefix
+  int* sC = sA + B + 1;   // [B+1] single-split item prefix
+
+
+  // The first of this thread's lengths.
+  const int per = (B + 511) / 512;
+  const int len0 = a.seq_lens[min((int)threadIdx.x * per, B - 1)];
+
+  // While the plan is built, load the table row, q and the appended rows of
+  // this workgroup's first item as it would be if every sequence filled its
+  // table row (exact for a uniform full-context batch; otherwise unused).  The
+  // loads are unconditional, with indices clamped into range, so that the
+  // waits placed for them count exactly.
+  const int ns_g = a.guess_ns;
+  const int b_raw = ns_g > 1 ? (int)__umulhi(blockIdx.x, a.guess_magic) : (int)blockIdx.x;
+  const int b_g = min(b_raw, B - 1);
+  const int s_g = (int)blockIdx.x - b_raw * ns_g;
+  const int n_g = ns_g > 1 ? (int)__umulhi((uint32_t)(a.max_blocks - s_g + ns_g - 1), a.guess_magic) : a.max_blocks;
+  ItemPrefetch pre;
+  pre.b = (a.max_blocks <= 128 && b_raw < B) ? b_raw : -1;
+  {
+    const int lane = threadIdx.x & 63, t = lane & 15, c = lane >> 4;
+    const int g = threadIdx.x >> 6;
+    const int32_t* bt = a.block_table + (size_t)b_g * a.max_blocks;
+    // entries past the row are clamped to its last one (never used)
+    pre.id0 = bt[min(lane, a.max_blocks - 1)];
+    pre.id1 = bt[min(64 + lane, a.max_blocks - 1)];
+    const uint16_t* qrow = a.q + ((size_t)b_g * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
+    pre.q0 = ld16(qrow + 8 * c);
+    pre.q1 = ld16(qrow + 32 + 8 * c);
+    pre.row = u32x4{0u, 0u, 0u, 0u};
+    if (kAppend)  // lanes 16-63 repeat lanes 0-15
+      pre.row = ld16(((lane & 8) ? a.v_new : a.k_new) + ((size_t)b_g * kKvHeads + g) * kHeadDim + 8 * (lane & 7));
+  }
+  const int L_g = a.seq_lens[b_g];
+  __builtin_amdgcn_sched_barrier(0);
+
+  // If the guessed sequence fills its table row, start the copies of the
+  // guessed item's first pages now, so that the plan overlaps them.
+  // They are used if the plan confirms the guess, else drained.
+  const DmaOffsets doff = dma_offsets(threadIdx.x & 63, threadIdx.x >> 6);
+  // the length and the table row are waited for here, so that no wait placed
+  // for them later includes the copies
+  asm volatile("" ::"v"(len0), "v"(pre.id0), "v"(pre.id1));
+  int prime_b = -1;
+  if (pre.b >= 0 && (L_g + kPageTokens - 1) / kPageTokens == a.max_blocks) {
+    const int g = threadIdx.x >> 6;
+    int32_t pages[kRing];
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int e = min(s_g + u * ns_g, a.max_blocks - 1);
+      pages[u] = e < 64 ? __builtin_amdgcn_readlane(pre.id0, e) : __builtin_amdgcn_readlane(pre.id1, e - 64);
+    }
+#pragma unroll
+    for (int u = 0; u < kRing; ++u)
+      if (u < n_g) issue_page(a, ring[g][u], pages[u], doff);
+    prime_b = pre.b;
+  }
+
+  const PlanLengths lens = plan_lengths(a.seq_lens, B, len0, sL);
+  const ItemPlan plan = plan_finish(lens, B, a.part_pages, sL, sA, sC, &plan_lds);
+  // values read back from LDS are the same in every lane: keep them scalar
+  const int ppu = __builtin_amdgcn_readfirstlane(plan.pp);
+  const int uns = __builtin_amdgcn_readfirstlane(plan.uniform_ns);
+
+  // Item blockIdx.x first.
+  int b = -1, s = 0, L = 0, nsplit = 1, n = 0;
+  if ((int)blockIdx.x < __builtin_amdgcn_readfirstlane(plan.n_items)) {
+    if (uns > 0 && pre.b >= 0 && __builtin_amdgcn_readfirstlane(plan.uniform_pages) == a.max_blocks &&
+        ppu == a.guess_pp) {
+      // every sequence fills its table row: the item is the guessed one
+      b = pre.b;
+      s = s_g;
+      L = L_g;
+      nsplit = ns_g;
+      n = n_g;
+    } else {
+      if (uns > 0) {
+        b = (int)blockIdx.x / uns;
+        s = (int)blockIdx.x - b * uns;
+      } else {
+        b = __builtin_amdgcn_readfirstlane(plan_lds.first[0]);
+        s = __builtin_amdgcn_readfirstlane(plan_lds.first[1]);
+      }
+      L = __builtin_amdgcn_readfirstlane(sL[b]);
+      nsplit = nsplit_of(L, ppu);
+      n = (L + kPageTokens - 1) / kPageTokens;
+      n = (n - s + nsplit - 1) / nsplit;  // pages s, s + nsplit, ... of the split (n <= 128)
+    }
+  }
+  bool primed = prime_b >= 0 && b == prime_b && s == s_g && nsplit == ns_g;
+  if (prime_b >= 0 && !primed) wait_vmcnt<0>();  // unused copies land before their slots are reused
+
+  // When the grid may hold fewer workgroups than items, later items come from
+  // a queue counter, so that workgroups busy with long splits take no further
+  // work.  Nothing of the plan is kept in registers across an item: the next
+  // item is derived from the plan in LDS.
+  while (b >= 0) {
+    if (s < nsplit) decode_item<kAppend>(a, b, s, nsplit, L, n, pre, primed, doff, ring, &last_split);
+    pre.b = -1;
+    primed = false;
+    b = -1;
+    if (!a.queue) break;
+    // Wave 0 claims the next item as soon as it is done; the first barrier also
+    // ensures every wave has read the previous next_item.
+    int fetched = 0;
+    if (threadIdx.x == 0)
+      fetched = (int)gridDim.x + __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (threadIdx.x == 0) next_item = fetched;
+    __syncthreads();
+    const int i = __builtin_amdgcn_readfirstlane(next_item);
+    const int n_multi = __builtin_amdgcn_readfirstlane(sA[B]);
+    const int n_items = n_multi + __builtin_amdgcn_readfirstlane(sC[B]);
+    if (i < n_items) {
+      const int pp = __builtin_amdgcn_readfirstlane(plan_lds.pp);
+      const int ns_u = __builtin_amdgcn_readfirstlane(plan_lds.uniform_ns);
+      if (ns_u > 0) {
+        b = i / ns_u;
+        s = i - b * ns_u;
+      } else if (i < n_multi) {
+        b = __builtin_amdgcn_readfirstlane(owner_of(sA, B, i));
+        s = i - __builtin_amdgcn_readfirstlane(sA[b]);
+      } else {
+        b = __builtin_amdgcn_readfirstlane(owner_of(sC, B, i - n_multi));
+        s = 0;
+      }
+      L = __builtin_amdgcn_readfirstlane(sL[b]);
+      nsplit = nsplit_of(L, pp);
+      n = (L + kPageTokens - 1) / kPageTokens;
+      n = (n - s + nsplit - 1) / nsplit;
+    }
+  }
+  // The last workgroup to leave resets the queue for the next call.
+  if (a.queue && threadIdx.x == 0) {
+    const int left = __hip_atomic_fetch_add(a.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == (int)gridDim.x - 1) {
+      __hip_atomic_store(a.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -450,11 +818,32 @@ hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t*
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int B, bool fused_append, hipStream_t stream) {
-  if (fused_append)
-    hipLaunchKernelGGL(decode_kernel<true>, dim3((unsigned)B * a.S), dim3(64 * kKvHeads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_kernel<false>, dim3((unsigned)B * a.S), dim3(64 * kKvHeads), 0, stream, a);
+// Dynamic LDS of a decode launch: the page ring and the plan's per-sequence arrays.
+static size_t decode_dynamic_lds_bytes(int B) {
+  return (size_t)kKvHeads * kRing * kSlotBytes + (3 * (size_t)B + 2) * sizeof(int);
+}
+
+size_t decode_lds_bytes(int B) { return decode_dynamic_lds_bytes(B) + sizeof(PlanLds) + 2 * sizeof(int); }
+
+int auto_split_pages(long long total_pages) {
+  return auto_pages_per_split((int)(total_pages < (1 << 30) ? total_pages : (1 << 30)));
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream) {
+  const size_t lds = decode_dynamic_lds_bytes(a.B);
+  if (fused_append) {
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_dynamic_lds_bytes(kMaxDecodeBatch));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
+  } else {
+    static const hipError_t attr =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_dynamic_lds_bytes(kMaxDecodeBatch));
+    if (attr != hipSuccess) return attr;
+    hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
+  }
   return hipGetLastError();
 }
 

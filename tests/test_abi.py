@@ -51,14 +51,17 @@ def test_status_strings(lib):
 
 
 def test_default_partition_and_workspace_sizes(lib):
-    pt = lib.pa_default_partition_tokens()
-    assert pt > 0 and pt % 16 == 0
-    # single split: no workspace
-    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 2048) == 0
-    assert lib.pa_decode_workspace_bytes(64, 32, 64, pt // 16, 0) == 0
-    # 8 splits of 256 tokens: part_o + part_m + part_l + one counter per sequence, each padded to 256 bytes
+    assert lib.pa_default_partition_tokens() == 0  # automatic split size
+    # single split: no partials, only the per-sequence counters and the queue counter
+    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 2048) == 256 + 256
+    assert lib.pa_decode_workspace_bytes(512, 32, 64, 8, 0) == 2048 + 256  # automatic splits have >= 8 pages
+    # automatic: partial rows for up to ceil(128 / 8) = 16 splits
+    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 0) == lib.pa_decode_workspace_bytes(64, 32, 64, 128, 128)
+    assert lib.pa_decode_workspace_bytes(5000, 32, 64, 128, 0) == 0  # batch above the plan limit
+    # 8 splits of 256 tokens: part_o + part_m + part_l + one counter per sequence + the queue,
+    # each padded to 256 bytes
     rows = 64 * 32 * 8
-    want = rows * 64 * 4 + 2 * (((rows * 4) + 255) // 256 * 256) + 256
+    want = rows * 64 * 4 + 2 * (((rows * 4) + 255) // 256 * 256) + 256 + 256
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 256) == want
     # partitions above 2048 tokens act as 2048
     assert lib.pa_decode_workspace_bytes(4, 32, 64, 256, 4096) == lib.pa_decode_workspace_bytes(4, 32, 64, 256, 2048) > 0
@@ -122,6 +125,7 @@ def test_decode_validation(lib):
     assert _decode(lib, ws=MIS, ws_bytes=need) == -6
     assert _decode(lib, q=MIS, ws=A, ws_bytes=need) == -6
     assert _decode(lib, B=0) == 0
+    assert _decode(lib, B=4097) == -2
 
 
 def _append_decode(lib, **kw):

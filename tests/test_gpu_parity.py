@@ -176,16 +176,28 @@ def test_page_permutation_bit_identical():
         assert torch.equal(x, y)
 
 
-def test_batch_invariance():
+@pytest.mark.parametrize("partition", [128, 512])
+def test_batch_invariance(partition):
+    """With a fixed partition a sequence's output does not depend on the rest of the batch."""
     lay = synth.fragmented(B=16, n_layers=1)
     d = Device(lay)
     d.append(0)
-    full = d.decode(0)
+    full = d.decode(0, partition_tokens=partition)
     x = d.inputs[0]
     for b in (0, 3, 7, 15):
         sub = ops.pa_decode(x["q"][b:b + 1].contiguous(), d.k_pool, d.v_pool, d.bt[0][b:b + 1].contiguous(),
-                            d.seq_lens[b:b + 1].contiguous(), lay.scale)
+                            d.seq_lens[b:b + 1].contiguous(), lay.scale, partition_tokens=partition)
         assert torch.equal(sub[0], full[b]), f"sequence {b} changes with the batch"
+
+
+def test_automatic_split_is_deterministic():
+    """The automatic split size is a function of the batch: repeated calls agree bit for bit."""
+    lay = synth.skewed(B=200, n_layers=1)
+    d = Device(lay)
+    d.append(0)
+    o1 = d.decode(0).clone()
+    o2 = d.decode(0)
+    assert torch.equal(o1, o2)
 
 
 def test_split_results_agree():
@@ -195,6 +207,22 @@ def test_split_results_agree():
     outs = {p: d.decode(0, partition_tokens=p).clone() for p in (16, 64, 256, 2048)}
     for p in (16, 64, 256):
         assert float((outs[p] - outs[2048]).abs().max()) <= 2e-3
+
+
+@pytest.mark.parametrize("partition", [0, 16, 2048])
+def test_uniform_batch_item_mapping(partition):
+    """Every sequence with the same page count (the plan's direct item mapping), with
+    more one-page splits than workgroups at partition 16 (the work queue in use)."""
+    lay = synth.full(B=8, n_layers=1)
+    d = Device(lay)
+    sample = [0, 3, 7]
+    pages = {b: synth.sequence_pages(d.k_pool, d.v_pool, lay, 0, b) for b in sample}
+    d.append(0)
+    out = d.decode(0, partition_tokens=partition)
+    torch.cuda.synchronize()
+    for b in sample:
+        kp, vp, _ = pages[b]
+        check_close(out[b].cpu().numpy(), oracle_sequence(d, 0, b, kp, vp), f"uniform seq {b} p{partition}")
 
 
 def test_length_one_is_the_v_row():
@@ -313,12 +341,15 @@ def test_workspace_reuse_and_counters_reset():
     outs = [ops.pa_decode(d.inputs[0]["q"], d.k_pool, d.v_pool, d.bt[0], d.seq_lens, lay.scale,
                           partition_tokens=part, workspace=ws).clone() for _ in range(3)]
     torch.cuda.synchronize()
-    # workspace layout: part_o, part_m, part_l (each padded to 256 bytes), then int32 counters [B]
+    # workspace layout: part_o, part_m, part_l, int32 counters [B], int32 queue [2], each padded
+    # to 256 bytes; 16 sequences x 128 one-page splits exceed the grid, so the queue is in use
     rnd = lambda x: (x + 255) // 256 * 256
     rows = lay.B * 32 * (lay.max_blocks * 16 // part)
     off_c = rnd(rows * 64 * 4) + 2 * rnd(rows * 4)
-    assert ws.numel() == off_c + rnd(lay.B * 4)
+    off_q = off_c + rnd(lay.B * 4)
+    assert ws.numel() == off_q + 256
     assert int(ws[off_c:off_c + lay.B * 4].view(torch.int32).abs().sum()) == 0
+    assert int(ws[off_q:off_q + 8].view(torch.int32).abs().sum()) == 0
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
     # other lengths on the same workspace
