@@ -132,7 +132,7 @@ def main():
     ap.add_argument("--config", default="full", help="workload: full, fragmented, skewed, large, small, tiny")
     ap.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-layers", type=int, default=4, help="layers of the workload the oracle runs on")
+    ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the workload the oracle runs on")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
@@ -254,7 +254,10 @@ def main():
     kv_step = lay.kv_bytes_per_step
     best_ms = ms_step if graph_ms is None else min(ms_step, graph_ms)
     value = kv_step / (best_ms * 1e-3) / 1e9
-    achieved = lay.kv_bytes_per_layer / (dec_ms_mean * 1e-3) / 1e9
+    # launch duration: the back-to-back stream timing divided by the launches
+    # (dispatch gaps included; rocprofv3's per-kernel average is the check)
+    launch_ms = ms_step / lay.n_layers
+    achieved = lay.kv_bytes_per_layer / (launch_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -275,7 +278,7 @@ def main():
             "seq_len_max": int(lay.seq_lens.max()),
             "layers": lay.n_layers,
             "kv_bytes_per_step": kv_step,
-            "partition_tokens": part or ops.pa_default_partition_tokens(),
+            "partition_tokens": part if part else "auto",
             "timing": "graph replay" if best_ms == graph_ms else "stream launches",
             "kv_dtype": "bf16",
             "parallelism": "single GPU",
@@ -295,7 +298,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": (measured_traffic() if (lay.name == "full" and args.partition == 0) else None),
             "bytes_per_launch": lay.kv_bytes_per_layer,
-            "mean_launch_us": round(dec_ms_mean * 1e3, 3),
+            "mean_launch_us": round(launch_ms * 1e3, 3),
+            "event_bracketed_launch_us": round(dec_ms_mean * 1e3, 3),
         },
         "cpu_baseline": cpu,
     }
