@@ -21,6 +21,9 @@ Sources (web pages describing the samir-vllm teaching engine):
   maps logical 16-token blocks to pages ([README] KV page pool item; [ARCH]).
 * Append: each decode step writes the one new token of a sequence into its
   page slot at its absolute position ([README] KV page pool item; [ARCH]).
+* Prefill fill: prefill writes the K and V rows of a sequence's prompt tokens
+  into that sequence's pages, through the same block table ([README] KV page
+  pool item: prefill fills prompt pages).
 * Decode attention: every query head reads its sequence's cached pages directly
   (no contiguous gather) and forms softmax-weighted sums of V ([README] paged
   decode attention item; [NF]).  The pages compute it with an FP32 online
@@ -38,6 +41,9 @@ Readings where the pages are silent (each one is listed in the design doc):
   * query head h uses KV head h // G with G = Hq / Hkv (contiguous groups).
   * in-page layout per plane: [16 tokens][Hkv][D].
   * L = 0: append skips the sequence; decode returns zeros for it.
+  * prefill fill writes n_b consecutive tokens of sequence b at positions
+    start_b .. start_b + n_b - 1; the pages' prefill is start_b = 0, and a
+    one-token fill at start_b = L - 1 is the append.
   * the split partial state is (m, l, o): m the maximum scaled score of the
     split in natural-log units, l = sum exp(s - m), o = (sum exp(s - m) v) / l.
 """
@@ -81,6 +87,36 @@ def append_ref(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new:
         written.add((page, slot))
         k_out[page, slot] = k_new[b]
         v_out[page, slot] = v_new[b]
+    return k_out, v_out
+
+
+def fill_ref(k_pool: np.ndarray, v_pool: np.ndarray, k_src: np.ndarray, v_src: np.ndarray,
+             block_table: np.ndarray, start, cu_tokens) -> Tuple[np.ndarray, np.ndarray]:
+    """Return copies of the pools with each sequence's run of tokens written (bit copy).
+
+    k_src/v_src: uint16 [T][Hkv][D], the tokens of all sequences one after another:
+    sequence b owns rows cu_tokens[b] .. cu_tokens[b+1]-1.  Row i of that range is the
+    token at position start[b] + i (start None: every start is 0), which lives in page
+    block_table[b][position // 16], slot position % 16.
+    """
+    k_out = np.array(k_pool, dtype=np.uint16, copy=True)
+    v_out = np.array(v_pool, dtype=np.uint16, copy=True)
+    num_pages, max_blocks = k_pool.shape[0], block_table.shape[1]
+    cu = np.asarray(cu_tokens, dtype=np.int64)
+    B = len(cu) - 1
+    st = np.zeros(B, np.int64) if start is None else np.asarray(start, dtype=np.int64)
+    written = set()
+    for b in range(B):
+        for i in range(int(cu[b + 1] - cu[b])):
+            pos = int(st[b]) + i
+            blk, slot = pos // PAGE_TOKENS, pos % PAGE_TOKENS
+            assert blk < max_blocks, "position beyond the block table"
+            page = int(block_table[b, blk])
+            assert 0 <= page < num_pages, "block table entry outside the pool"
+            assert (page, slot) not in written, "two tokens written into the same slot"
+            written.add((page, slot))
+            k_out[page, slot] = k_src[cu[b] + i]
+            v_out[page, slot] = v_src[cu[b] + i]
     return k_out, v_out
 
 
