@@ -65,6 +65,7 @@ extern "C" {
 #define PA_Q_HEADS 32
 #define PA_MAX_BLOCKS_LIMIT 4096
 #define PA_MAX_DECODE_BATCH 4096
+#define PA_MAX_FILL_BATCH 4096
 
 enum pa_status {
   PA_OK = 0,
@@ -98,6 +99,32 @@ const char* pa_status_string(int status);
 int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
               const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
               int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
+
+/*
+ * pa_fill - write a run of consecutive tokens of every sequence into its pages
+ * (prefill).  ([README] KV page pool item: prefill fills prompt pages, through
+ * the same per-(sequence, layer) block table that decode reads.)
+ *
+ * Sequence b's run is rows cu_tokens[b] .. cu_tokens[b+1]-1 of k_src / v_src;
+ * row i of it is the token at position p = start[b] + i and is bit-copied to
+ * k_pool[block_table[b][p/16]][p%16] (likewise V).  The pages' prefill is
+ * start = 0 (the whole prompt); a one-token run at position L-1 is pa_append.
+ *
+ *   k_src, v_src  bf16 [T][Hkv][D], the runs one after another
+ *   k_pool, v_pool bf16 [num_pages][16][Hkv][D] (written)
+ *   block_table   int32 [B][max_blocks] of one layer
+ *   start         int32 [B], or NULL for all 0
+ *   cu_tokens     int32 [B+1]: cu_tokens[0] = 0, nondecreasing, cu_tokens[B] = T
+ *   B             0 .. PA_MAX_FILL_BATCH; T total rows (0 .. 2^31-17)
+ * The caller assigns every page the runs reach before the call.  Rows whose
+ * position is negative or past the table, or whose table entry is outside
+ * [0, num_pages), are not written.  Runs must not overlap in the pool.
+ * Returns PA_OK, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_NULL, PA_ERR_ALIGN
+ * or PA_ERR_LAUNCH; nothing is launched for B == 0 or T == 0.
+ */
+int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint16_t* v_pool,
+            const int32_t* block_table, int32_t max_blocks, const int32_t* start, const int32_t* cu_tokens,
+            int32_t B, int64_t T, int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
 
 /*
  * Bytes of workspace pa_decode and pa_append_decode need for these sizes

@@ -118,6 +118,33 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
   return PA_OK;
 }
 
+int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint16_t* v_pool,
+            const int32_t* block_table, int32_t max_blocks, const int32_t* start, const int32_t* cu_tokens,
+            int32_t B, int64_t T, int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream) {
+  if (B < 0 || B > PA_MAX_FILL_BATCH || T < 0 || T > INT32_MAX - 16 || max_blocks <= 0 ||
+      max_blocks > PA_MAX_BLOCKS_LIMIT || num_pages <= 0 || num_pages > INT32_MAX)
+    return PA_ERR_SHAPE;
+  if (Hkv <= 0 || D <= 0) return PA_ERR_SHAPE;
+  if (Hkv != pa::kKvHeads || D != pa::kHeadDim) return PA_ERR_UNSUPPORTED;
+  if (B == 0 || T == 0) return PA_OK;
+  if (!k_src || !v_src || !k_pool || !v_pool || !block_table || !cu_tokens) return PA_ERR_NULL;
+  if (misaligned(k_src) || misaligned(v_src) || misaligned(k_pool) || misaligned(v_pool)) return PA_ERR_ALIGN;
+  pa::FillArgs a;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.start = start;
+  a.cu_tokens = cu_tokens;
+  a.B = B;
+  a.max_blocks = max_blocks;
+  a.T = (int)T;
+  a.num_pages = (int)num_pages;
+  if (pa::launch_fill(a, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
                                  int32_t partition_tokens) {
   if (B <= 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return 0;

@@ -58,6 +58,22 @@ struct MergeArgs {
   int skip_single;  // 1 inside pa_decode: rows with one split were written by the decode kernel
 };
 
+struct FillArgs {
+  const uint16_t* k_src;  // [T][Hkv][D]
+  const uint16_t* v_src;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+  const int32_t* block_table;  // [B][max_blocks]
+  const int32_t* start;        // [B] first position of each run; NULL: all 0
+  const int32_t* cu_tokens;    // [B+1] run b is rows cu_tokens[b] .. cu_tokens[b+1]-1
+  int B;
+  int max_blocks;
+  int T;
+  int num_pages;
+};
+
+hipError_t launch_fill(const FillArgs& a, hipStream_t stream);
+
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);

@@ -17,6 +17,8 @@
 
 #include "pa_kernels.h"
 
+#include <algorithm>
+
 namespace pa {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -63,6 +65,60 @@ __global__ __launch_bounds__(256) void append_kernel(const uint16_t* __restrict_
   const size_t src = (size_t)b * kRowElems + lane * 8;
   *reinterpret_cast<u32x4*>(k_pool + dst) = ld16(k_new + src);
   *reinterpret_cast<u32x4*>(v_pool + dst) = ld16(v_new + src);
+}
+
+// ---------------------------------------------------------------------------
+// pa_fill: a run of consecutive tokens per sequence into its pages.  Each wave
+// moves 4 consecutive source rows per iteration (16 bytes of the K row and of
+// the V row per lane); the run boundaries are staged in LDS and the sequence of
+// a token found by binary search.  Rows whose position or page falls outside
+// the table or the pool are skipped (the caller's contract excludes them).
+
+constexpr int kFillRowsPerWave = 4;
+
+__global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
+  extern __shared__ int s_cu[];  // [B + 1]
+  for (int i = threadIdx.x; i <= a.B; i += 256) s_cu[i] = a.cu_tokens[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int nchunk = (a.T + kFillRowsPerWave - 1) / kFillRowsPerWave;
+  for (int c = blockIdx.x * 4 + (threadIdx.x >> 6); c < nchunk; c += gridDim.x * 4) {
+    const int t0 = c * kFillRowsPerWave;
+    int lo = 0, hi = a.B;  // largest b with cu[b] <= t0, for cu[0] = 0 <= t0 < cu[B] = T
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    int b = __builtin_amdgcn_readfirstlane(lo);
+    u32x4 kr[kFillRowsPerWave], vr[kFillRowsPerWave];
+    size_t dst[kFillRowsPerWave];
+    bool ok[kFillRowsPerWave];
+#pragma unroll
+    for (int u = 0; u < kFillRowsPerWave; ++u) {
+      const int t = t0 + u;
+      ok[u] = false;
+      dst[u] = 0;
+      if (t < a.T) {
+        while (b + 1 < a.B && s_cu[b + 1] <= t) ++b;  // runs may be empty
+        const int pos = (a.start ? a.start[b] : 0) + (t - s_cu[b]);
+        if (pos >= 0 && (pos >> 4) < a.max_blocks) {
+          const int page = a.block_table[(size_t)b * a.max_blocks + (pos >> 4)];
+          if (page >= 0 && page < a.num_pages) {
+            ok[u] = true;
+            dst[u] = ((size_t)page * kPageTokens + (pos & 15)) * kRowElems + lane * 8;
+          }
+        }
+        kr[u] = ld16(a.k_src + (size_t)t * kRowElems + lane * 8);
+        vr[u] = ld16(a.v_src + (size_t)t * kRowElems + lane * 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFillRowsPerWave; ++u)
+      if (ok[u]) {
+        __builtin_nontemporal_store(kr[u], reinterpret_cast<u32x4*>(a.k_pool + dst[u]));
+        __builtin_nontemporal_store(vr[u], reinterpret_cast<u32x4*>(a.v_pool + dst[u]));
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -844,6 +900,17 @@ hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipSt
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill(const FillArgs& a, hipStream_t stream) {
+  const int nchunk = (a.T + kFillRowsPerWave - 1) / kFillRowsPerWave;
+  int cus = 256, dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    cus = n;
+  const int grid = std::min((nchunk + 3) / 4, cus * 8);
+  hipLaunchKernelGGL(fill_kernel, dim3(grid), dim3(256), (a.B + 1) * sizeof(int), stream, a);
   return hipGetLastError();
 }
 

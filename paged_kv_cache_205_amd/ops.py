@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN"}
-EXPORTS = ("pa_status_string", "pa_append", "pa_decode_workspace_bytes",
+EXPORTS = ("pa_status_string", "pa_append", "pa_fill", "pa_decode_workspace_bytes",
            "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_merge")
 
 _lib = None
@@ -44,6 +44,8 @@ def load() -> ctypes.CDLL:
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_append.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I64, P]
     lib.pa_append.restype = ctypes.c_int
+    lib.pa_fill.argtypes = [P, P, P, P, P, I32, P, P, I32, I64, I32, I32, I64, P]
+    lib.pa_fill.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_default_partition_tokens.argtypes = []
@@ -94,6 +96,19 @@ def pa_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, stream=None) 
                        block_table.shape[1], _ptr(seq_lens, torch.int32, "seq_lens"), B, Hkv, D,
                        k_pool.shape[0], _stream(k_pool.device, stream))
     _check("pa_append", st)
+
+
+def pa_fill(k_src, v_src, k_pool, v_pool, block_table, cu_tokens, start=None, stream=None) -> None:
+    """k_src/v_src bf16 [T][8][64] (runs one after another); cu_tokens int32 [B+1] on the device,
+    with T = cu_tokens[B] (the host's T is the rows of k_src); start int32 [B] or None (all 0)."""
+    T, Hkv, D = k_src.shape
+    B = cu_tokens.shape[0] - 1
+    lib = load()
+    st = lib.pa_fill(_bf16(k_src, "k_src"), _bf16(v_src, "v_src"), _bf16(k_pool, "k_pool"), _bf16(v_pool, "v_pool"),
+                     _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+                     _ptr(start, torch.int32, "start"), _ptr(cu_tokens, torch.int32, "cu_tokens"), B, T, Hkv, D,
+                     k_pool.shape[0], _stream(k_pool.device, stream))
+    _check("pa_fill", st)
 
 
 def pa_decode_workspace_bytes(B: int, max_blocks: int, partition_tokens: int = 0, Hq: int = 32, D: int = 64) -> int:

@@ -181,3 +181,32 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "libpa.so"))
     with pytest.raises(RuntimeError, match="missing"):
         ops.load()
+
+
+def _fill(lib, **kw):
+    args = dict(ks=A, vs=A, k=A, v=A, bt=A, max_blocks=128, start=None, cu=A, B=4, T=100, Hkv=8, D=64,
+                num_pages=1024, stream=None)
+    args.update(kw)
+    return lib.pa_fill(args["ks"], args["vs"], args["k"], args["v"], args["bt"], args["max_blocks"], args["start"],
+                       args["cu"], args["B"], args["T"], args["Hkv"], args["D"], args["num_pages"], args["stream"])
+
+
+def test_fill_validation(lib):
+    assert _fill(lib, B=-1) == -2
+    assert _fill(lib, B=4097) == -2
+    assert _fill(lib, T=-1) == -2
+    assert _fill(lib, T=1 << 31) == -2
+    assert _fill(lib, max_blocks=0) == -2
+    assert _fill(lib, max_blocks=4097) == -2
+    assert _fill(lib, num_pages=0) == -2
+    assert _fill(lib, Hkv=4) == -3
+    assert _fill(lib, D=128) == -3
+    assert _fill(lib, ks=None) == -1
+    assert _fill(lib, cu=None) == -1
+    assert _fill(lib, bt=None) == -1
+    assert _fill(lib, ks=MIS) == -6
+    assert _fill(lib, v=MIS) == -6
+    # nothing to do: no launch
+    assert _fill(lib, B=0) == 0
+    assert _fill(lib, T=0) == 0
+    assert _fill(lib, B=0, ks=None, cu=None) == 0

@@ -1,0 +1,135 @@
+"""pa_fill on the GPU against the oracle's fill_ref: bit-exact on whole pools.
+
+Cases: ragged runs with empty ones and starts that are not page-aligned, the
+largest batch (4096 runs), the full-size prefill (64 prompts of 2047 tokens),
+one-token runs against pa_append, fill followed by decode, and table entries
+outside the pool (skipped, never written).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode_ref, fill_ref
+from paged_kv_cache_205_amd import ops
+from tests.helpers import check_close, say
+from tests.test_oracle import rand_bits
+from tests.test_oracle_fill import fill_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.load()
+
+
+def dev_bf16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_fill(kp, vp, ks, vs, bt, st, cu, use_start=True):
+    k, v = dev_bf16(kp), dev_bf16(vp)
+    say(f"pa_fill B={len(cu) - 1} T={int(cu[-1])} pages={kp.shape[0]}")
+    ops.pa_fill(dev_bf16(ks), dev_bf16(vs), k, v, torch.from_numpy(bt).cuda(), torch.from_numpy(cu).cuda(),
+                start=torch.from_numpy(st).cuda() if use_start else None)
+    torch.cuda.synchronize()
+    return host_bits(k), host_bits(v)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_ragged_runs_bit_exact(seed):
+    rng = np.random.default_rng(100 + seed)
+    lens = [0, 1, 15, 16, 17, 33, 0, 250] + rng.integers(0, 200, size=8).tolist()
+    starts = [0, 0, 1, 16, 15, 7, 3, 0] + rng.integers(0, 60, size=8).tolist()
+    kp, vp, ks, vs, bt, st, cu = fill_case(seed, lens, starts, Hkv=8, D=64, max_blocks=20)
+    k_ref, v_ref = fill_ref(kp, vp, ks, vs, bt, st, cu)
+    k_got, v_got = run_fill(kp, vp, ks, vs, bt, st, cu)
+    assert np.array_equal(k_got, k_ref) and np.array_equal(v_got, v_ref)
+
+
+def test_prompts_from_position_zero_without_start():
+    lens = [37, 1, 128, 0, 64]
+    kp, vp, ks, vs, bt, st, cu = fill_case(3, lens, None, Hkv=8, D=64, max_blocks=8)
+    k_ref, v_ref = fill_ref(kp, vp, ks, vs, bt, None, cu)
+    k_got, v_got = run_fill(kp, vp, ks, vs, bt, st, cu, use_start=False)
+    assert np.array_equal(k_got, k_ref) and np.array_equal(v_got, v_ref)
+
+
+def test_largest_batch():
+    rng = np.random.default_rng(4)
+    lens = rng.integers(0, 4, size=4096).tolist()
+    starts = rng.integers(0, 30, size=4096).tolist()
+    kp, vp, ks, vs, bt, st, cu = fill_case(4, lens, starts, Hkv=8, D=64, max_blocks=3, spare=0)
+    k_ref, v_ref = fill_ref(kp, vp, ks, vs, bt, st, cu)
+    k_got, v_got = run_fill(kp, vp, ks, vs, bt, st, cu)
+    assert np.array_equal(k_got, k_ref) and np.array_equal(v_got, v_ref)
+
+
+def test_full_size_prefill():
+    """64 prompts of 2047 tokens into a 128-block table each (the decode step then
+    appends position 2047)."""
+    lens = [2047] * 64
+    kp, vp, ks, vs, bt, st, cu = fill_case(5, lens, None, Hkv=8, D=64, max_blocks=128, spare=16)
+    k_ref, v_ref = fill_ref(kp, vp, ks, vs, bt, None, cu)
+    k_got, v_got = run_fill(kp, vp, ks, vs, bt, st, cu, use_start=False)
+    assert np.array_equal(k_got, k_ref) and np.array_equal(v_got, v_ref)
+
+
+def test_one_token_runs_match_append():
+    lens_after = np.array([1, 16, 17, 2048, 300], np.int32)
+    kp, vp, ks, vs, bt, st, cu = fill_case(6, [1] * 5, (lens_after - 1).tolist(), Hkv=8, D=64, max_blocks=128)
+    k1, v1 = dev_bf16(kp), dev_bf16(vp)
+    ops.pa_append(dev_bf16(ks), dev_bf16(vs), k1, v1, torch.from_numpy(bt).cuda(), torch.from_numpy(lens_after).cuda())
+    k2, v2 = run_fill(kp, vp, ks, vs, bt, st, cu)
+    assert np.array_equal(host_bits(k1), k2) and np.array_equal(host_bits(v1), v2)
+
+
+def test_fill_then_decode():
+    lens = [1, 15, 16, 100, 513]
+    kp, vp, ks, vs, bt, st, cu = fill_case(7, lens, None, Hkv=8, D=64, max_blocks=33)
+    k, v = dev_bf16(kp), dev_bf16(vp)
+    btd, cud = torch.from_numpy(bt).cuda(), torch.from_numpy(cu).cuda()
+    ops.pa_fill(dev_bf16(ks), dev_bf16(vs), k, v, btd, cud)
+    q = dev_bf16(rand_bits(np.random.default_rng(8), (5, 32, 64)))
+    out = ops.pa_decode(q, k, v, btd, torch.tensor(lens, dtype=torch.int32, device="cuda"), 0.125)
+    torch.cuda.synchronize()
+    k_ref, v_ref = fill_ref(kp, vp, ks, vs, bt, None, cu)
+    ref = decode_ref(host_bits(q), k_ref, v_ref, bt, np.array(lens, np.int32), 0.125)
+    for b in range(5):
+        check_close(out[b].cpu().numpy(), ref[b], f"fill+decode seq {b}")
+
+
+def test_entries_outside_the_pool_are_skipped():
+    lens, starts = [40, 20], [0, 5]
+    kp, vp, ks, vs, bt, st, cu = fill_case(9, lens, starts, Hkv=8, D=64, max_blocks=4)
+    bad = bt.copy()
+    bad[0, 1] = -1               # positions 16..31 of run 0: no page
+    bad[1, 1] = kp.shape[0] + 7  # positions 16..24 of run 1: past the pool
+    k_got, v_got = run_fill(kp, vp, ks, vs, bad, st, cu)
+    # the oracle on the rows that have a valid page: runs cut at the bad blocks
+    keep = [(0, 0, 16), (0, 32, 40), (1, 5, 16)]
+    k_ref, v_ref = kp.copy(), vp.copy()
+    for b, p0, p1 in keep:
+        for p in range(p0, p1):
+            row = cu[b] + p - starts[b]
+            k_ref[bad[b, p // 16], p % 16] = ks[row]
+            v_ref[bad[b, p // 16], p % 16] = vs[row]
+    assert np.array_equal(k_got, k_ref) and np.array_equal(v_got, v_ref)
+
+
+def test_empty_calls():
+    kp = np.zeros((4, 16, 8, 64), np.uint16)
+    k = dev_bf16(kp)
+    src = torch.empty((0, 8, 64), dtype=torch.bfloat16, device="cuda")
+    ops.pa_fill(src, src, k, k, torch.zeros((2, 4), dtype=torch.int32, device="cuda"),
+                torch.zeros(3, dtype=torch.int32, device="cuda"))
+    ops.pa_fill(src, src, k, k, torch.zeros((0, 4), dtype=torch.int32, device="cuda"),
+                torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(k.view(torch.int16))) == 0
