@@ -11,8 +11,12 @@ at 2048 tokens, 16 layers, 32 query / 8 KV heads, head dim 64, 16-token pages
 
 Prints one JSON line: effective KV GB/s for the whole step (KV bytes the
 attention must read / step time), µs per step, the roofline of the decode kernel
-(algorithmic bytes per launch / mean launch time from HIP events) and the FP64
-CPU oracle timed on a bounded sample of the same workload.
+(algorithmic bytes per launch / launch time) and the FP64 CPU oracle timed on a
+bounded sample of the same workload.
+
+``--op fill`` measures the prefill page fill instead: every layer's prompt rows
+(positions 0..L-2 of each sequence of the workload, packed one sequence after
+another) written into the pool with one ``pa_fill`` per layer.
 """
 from __future__ import annotations
 
@@ -37,15 +41,17 @@ def log(*a):
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_full_b64_l2048.md")
+FILL_PROFILE = os.path.join(ROOT, "profiles", "fill_kernel_full_b64_l2047.md")
+FILL_METRIC = "prefill page fill: effective GB/s (K/V rows read + written), µs/step at batch 64×2047"
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source (pa_kernels.hip, pa_api.cpp); else None."""
+def measured_traffic(profile=None):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (pa_kernels.hip, pa_api.cpp); else None."""
     import hashlib
     import re
     try:
-        text = open(TRAFFIC_PROFILE).read()
+        text = open(profile or TRAFFIC_PROFILE).read()
     except OSError:
         return None
     m_sha = re.search(r"sha256[^`]*`([0-9a-f]{64})`", text)
@@ -57,6 +63,133 @@ def measured_traffic():
         with open(os.path.join(ROOT, "paged_kv_cache_205_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return int(m_tr.group(1)) if h.hexdigest() == m_sha.group(1) else None
+
+
+def _oracle_fill(item):
+    """fill_ref for one (layer, sequence) of the fill sample; returns the rows written."""
+    from oracle import fill_ref
+    l, b = item
+    d = _CPU[("fill", l)]
+    kp, vp, bt = d["pages"][b]
+    c0, c1 = int(d["cu"][b]), int(d["cu"][b + 1])
+    fill_ref(kp, vp, d["k"][c0:c1], d["v"][c0:c1], bt, None, np.array([0, c1 - c0], np.int32))
+    return c1 - c0
+
+
+def cpu_baseline_fill(lay, n_layers: int, workers: int):
+    """Time the oracle's fill on the first n_layers layers (each sequence into its own pages)."""
+    import torch
+    from paged_kv_cache_205_amd import synth
+    torch.set_num_threads(1)
+    layers = list(range(min(n_layers, lay.n_layers)))
+    for l in layers:
+        ks, vs, cu = synth.prefill_inputs(lay, l, "cpu")
+        pages = {}
+        for b in range(lay.B):
+            n = max(synth.nblocks(int(lay.seq_lens[b]) - 1), 1)
+            nan = np.full((n, 16, 8, 64), 0x7FC0, np.uint16)
+            pages[b] = (nan, nan.copy(), np.arange(n, dtype=np.int32)[None])
+        _CPU[("fill", l)] = dict(pages=pages, k=synth.bits(ks), v=synth.bits(vs), cu=cu.numpy())
+    items = [(l, b) for l in layers for b in range(lay.B)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        rows = sum(pool.map(_oracle_fill, items, chunksize=1))
+    tw = time.perf_counter() - t0
+    return {
+        "value": round(rows * 4096 / tw / 1e9, 6),  # 2 KiB of K and V read and 2 KiB written per row
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"layers 0..{layers[-1]} of the same prefill, all {lay.B} sequences each ({rows} rows): "
+                  f"fill_ref (NumPy) in {workers} worker processes, {tw:.1f} s wall",
+        "seconds": round(tw, 2),
+    }
+
+
+def bench_fill(args, lay):
+    """One step = one pa_fill per layer of every sequence's prompt rows."""
+    cpu = None
+    if not args.no_cpu:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"cpu baseline (fill): oracle on {workers} workers ...")
+        cpu = cpu_baseline_fill(lay, args.cpu_layers, workers)
+    import torch
+    from paged_kv_cache_205_amd import ops, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load()
+    dev = "cuda"
+    shape = (lay.num_pages, 16, 8, 64)
+    k_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    src = [synth.prefill_inputs(lay, l, dev) for l in range(lay.n_layers)]
+    T = int(src[0][0].shape[0])
+    bytes_launch = sum(int(x[0].shape[0]) for x in src) * 4096 // lay.n_layers
+    if args.calib_copy_mib:
+        a = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        torch.empty_like(a).copy_(a)
+        del a
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(lay.n_layers):
+            ks, vs, cu = src[l]
+            ops.pa_fill(ks, vs, k_pool, v_pool, bt[l], cu)
+
+    for _ in range(args.warmup):
+        step()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    launch_ms = ms_step / lay.n_layers
+    value = bytes_launch * lay.n_layers / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": FILL_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"prefill fill of {lay.name}: B={lay.B} prompts of L-1 tokens, {lay.n_layers} layers, "
+                        f"8 kv heads, D=64, 16-token BF16 pages",
+            "batch": lay.B,
+            "rows_per_layer": T,
+            "layers": lay.n_layers,
+            "bytes_per_step": bytes_launch * lay.n_layers,
+            "timing": "stream launches",
+            "parallelism": "single GPU",
+        },
+        "us_per_step": round(ms_step * 1e3, 2),
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "fill_kernel (one launch per layer)",
+            "bound": "hbm",
+            "achieved": round(bytes_launch / (launch_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bytes_launch / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(FILL_PROFILE) if lay.name == "full" else None,
+            "bytes_per_launch": bytes_launch,
+            "mean_launch_us": round(launch_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
 
 
 # ----------------------------------------------------------------------------
@@ -134,6 +267,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the workload the oracle runs on")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
+    ap.add_argument("--op", choices=("decode", "fill"), default="decode",
+                    help="decode: the decode step (default); fill: the prefill page fill")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -145,6 +280,9 @@ def main():
 
     from paged_kv_cache_205_amd import synth
     lay = synth.get(args.config)
+    if args.op == "fill":
+        bench_fill(args, lay)
+        return
 
     cpu = None
     if not args.no_cpu:

@@ -312,6 +312,29 @@ def make_pools(lay: Layout, device="cpu", layers: Optional[List[int]] = None,
     return k_pool, v_pool
 
 
+def prefill_inputs(lay: Layout, layer: int, device="cpu", chunk_rows: int = 1 << 22):
+    """One layer's prompt rows packed as a prefill fill takes them.
+
+    Returns (k_src, v_src, cu_tokens): bf16 [T][8][64] holding the values that
+    ``make_pools`` puts at positions 0..L-2 of every sequence (same generators,
+    same (sequence, position) order), and int32 [B+1] run boundaries with
+    run b of length max(L_b - 1, 0).
+    """
+    dev = torch.device(device)
+    n = np.maximum(lay.seq_lens.astype(np.int64) - 1, 0)
+    cu = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    T = int(cu[-1])
+    ks, vs = [], []
+    for c, start in enumerate(range(0, T, chunk_rows)):
+        k, v = _layer_values(lay, layer, min(chunk_rows, T - start), c, dev)
+        ks.append(k)
+        vs.append(v)
+    empty = torch.empty((0, ROW_ELEMS), dtype=torch.bfloat16, device=dev)
+    k_src = (torch.cat(ks) if ks else empty).view(T, HKV, HEAD_DIM)
+    v_src = (torch.cat(vs) if vs else empty).view(T, HKV, HEAD_DIM)
+    return k_src, v_src, torch.from_numpy(cu).to(dev)
+
+
 def layer_pages(lay: Layout, layer: int, device="cpu", chunk_rows: int = 1 << 22):
     """Only the pages of one layer, renumbered 0..n-1: (k_pages, v_pages, block_table).
 

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle import decode_ref, fill_ref
-from paged_kv_cache_205_amd import ops
+from paged_kv_cache_205_amd import ops, synth
 from tests.helpers import check_close, say
 from tests.test_oracle import rand_bits
 from tests.test_oracle_fill import fill_case
@@ -133,3 +133,19 @@ def test_empty_calls():
                 torch.zeros(1, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
     assert int(torch.count_nonzero(k.view(torch.int16))) == 0
+
+
+def test_filling_every_layer_rebuilds_the_prefilled_pool():
+    """The small workload's prompt rows of all 16 layers, filled into a NaN pool, give
+    exactly the pool the generator builds directly (a 4096-page shared pool)."""
+    lay = synth.small()
+    k_ref, v_ref = synth.make_pools(lay, "cuda")
+    k = torch.full_like(k_ref, float("nan"))
+    v = torch.full_like(v_ref, float("nan"))
+    bt = torch.from_numpy(lay.block_tables).cuda()
+    for l in range(lay.n_layers):
+        ks, vs, cu = synth.prefill_inputs(lay, l, "cuda")
+        ops.pa_fill(ks, vs, k, v, bt[l], cu)
+    torch.cuda.synchronize()
+    assert torch.equal(k.view(torch.int16), k_ref.view(torch.int16))
+    assert torch.equal(v.view(torch.int16), v_ref.view(torch.int16))

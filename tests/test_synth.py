@@ -90,3 +90,17 @@ def test_layer_pages_match_make_pools():
                                kl[torch.from_numpy(btl[b, :n].astype(np.int64))].view(torch.int16))
             assert torch.equal(v[torch.from_numpy(lay.block_tables[l, b, :n].astype(np.int64))].view(torch.int16),
                                vl[torch.from_numpy(btl[b, :n].astype(np.int64))].view(torch.int16))
+
+
+def test_prefill_inputs_fill_to_the_generated_pool():
+    """The packed prompt rows, written by the oracle's fill, rebuild make_pools' pages."""
+    from oracle import fill_ref
+    lay = synth.small()
+    kp, vp = synth.make_pools(lay, "cpu", layers=[0, 5])
+    nan = synth.bits(torch.full_like(kp, float("nan")))
+    k2, v2 = nan, nan.copy()
+    for l in (0, 5):
+        ks, vs, cu = synth.prefill_inputs(lay, l)
+        assert ks.shape[0] == int(np.maximum(lay.seq_lens - 1, 0).sum()) == int(cu[-1])
+        k2, v2 = fill_ref(k2, v2, synth.bits(ks), synth.bits(vs), lay.block_tables[l], None, cu.numpy())
+    assert np.array_equal(k2, synth.bits(kp)) and np.array_equal(v2, synth.bits(vp))
