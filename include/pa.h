@@ -74,7 +74,10 @@ enum pa_status {
   PA_ERR_UNSUPPORTED = -3, /* dims other than Hq=32, Hkv=8, D=64 */
   PA_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required */
   PA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch */
-  PA_ERR_ALIGN = -6        /* an array pointer is not 16-byte aligned */
+  PA_ERR_ALIGN = -6,       /* an array pointer is not 16-byte aligned */
+  PA_ERR_REJECTED = -7,    /* pa_sched: the request's budget exceeds the whole pool */
+  PA_ERR_BUDGET = -8,      /* pa_sched: growth beyond the request's reserved prefix */
+  PA_ERR_STATE = -9        /* pa_sched: the request is not active */
 };
 
 /* Human-readable name of a status code (static string). */

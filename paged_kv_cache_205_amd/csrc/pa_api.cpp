@@ -94,6 +94,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or too small";
     case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
     case PA_ERR_ALIGN: return "PA_ERR_ALIGN: an array pointer is not 16-byte aligned";
+    case PA_ERR_REJECTED: return "PA_ERR_REJECTED: the request's page budget exceeds the whole pool";
+    case PA_ERR_BUDGET: return "PA_ERR_BUDGET: growth beyond the request's reserved prefix";
+    case PA_ERR_STATE: return "PA_ERR_STATE: the request is not active";
     default: return "unknown pa status";
   }
 }

@@ -18,9 +18,13 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
-          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN"}
+          -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN", -7: "PA_ERR_REJECTED",
+          -8: "PA_ERR_BUDGET", -9: "PA_ERR_STATE"}
 EXPORTS = ("pa_status_string", "pa_append", "pa_fill", "pa_decode_workspace_bytes",
-           "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_merge")
+           "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_merge",
+           "pa_sched_budget_pages", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_admit",
+           "pa_sched_grow", "pa_sched_block_table", "pa_sched_finish", "pa_sched_decode_batch",
+           "pa_sched_get_stats")
 
 _lib = None
 
@@ -56,6 +60,26 @@ def load() -> ctypes.CDLL:
     lib.pa_append_decode.restype = ctypes.c_int
     lib.pa_merge.argtypes = [P, P, P, P, I32, P, I32, I32, I32, I32, P]
     lib.pa_merge.restype = ctypes.c_int
+    lib.pa_sched_budget_pages.argtypes = [I32, I32, I32, I32, ctypes.POINTER(I64)]
+    lib.pa_sched_budget_pages.restype = ctypes.c_int
+    lib.pa_sched_create.argtypes = [I64, I32, I32, I32, ctypes.POINTER(P)]
+    lib.pa_sched_create.restype = ctypes.c_int
+    lib.pa_sched_destroy.argtypes = [P]
+    lib.pa_sched_destroy.restype = None
+    lib.pa_sched_submit.argtypes = [P, I32, I32, ctypes.POINTER(I64)]
+    lib.pa_sched_submit.restype = ctypes.c_int
+    lib.pa_sched_admit.argtypes = [P, ctypes.POINTER(I64), I32, ctypes.POINTER(I32)]
+    lib.pa_sched_admit.restype = ctypes.c_int
+    lib.pa_sched_grow.argtypes = [P, I64, I32]
+    lib.pa_sched_grow.restype = ctypes.c_int
+    lib.pa_sched_block_table.argtypes = [P, I64, I32, ctypes.POINTER(I32), I32]
+    lib.pa_sched_block_table.restype = ctypes.c_int
+    lib.pa_sched_finish.argtypes = [P, I64]
+    lib.pa_sched_finish.restype = ctypes.c_int
+    lib.pa_sched_decode_batch.argtypes = [P, I32]
+    lib.pa_sched_decode_batch.restype = ctypes.c_int
+    lib.pa_sched_get_stats.argtypes = [P, ctypes.POINTER(SchedStats)]
+    lib.pa_sched_get_stats.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -180,3 +204,83 @@ def pa_merge(part_o, part_m, part_l, seq_lens=None, partition_tokens: int = 0, o
                       _stream(part_o.device, stream))
     _check("pa_merge", st)
     return out
+
+
+# ----------------------------------------------------------------------------
+# page-budget admission and lazy page assignment (include/pa_sched.h; host only)
+
+
+class SchedStats(ctypes.Structure):
+    _fields_ = [("pool_pages", ctypes.c_int64), ("free_pages", ctypes.c_int64), ("assigned_pages", ctypes.c_int64),
+                ("peak_assigned_pages", ctypes.c_int64), ("credits_free", ctypes.c_int64),
+                ("active", ctypes.c_int32), ("waiting", ctypes.c_int32), ("peak_active", ctypes.c_int32),
+                ("largest_decode_batch", ctypes.c_int32), ("admission_waits", ctypes.c_int64),
+                ("rejected", ctypes.c_int64), ("completed", ctypes.c_int64)]
+
+
+def sched_budget_pages(prompt_tokens: int, max_new_tokens: int, context: int = 2048, n_layers: int = 16) -> int:
+    out = ctypes.c_int64()
+    _check("pa_sched_budget_pages", load().pa_sched_budget_pages(prompt_tokens, max_new_tokens, context, n_layers,
+                                                                 ctypes.byref(out)))
+    return out.value
+
+
+class Scheduler:
+    """Thin owner of a pa_sched object: arguments are passed through as they are."""
+
+    def __init__(self, pool_pages: int, n_layers: int = 16, context: int = 2048, static: bool = False):
+        self._h = None
+        self._lib = load()
+        h = ctypes.c_void_p()
+        _check("pa_sched_create", self._lib.pa_sched_create(pool_pages, n_layers, context, int(static), ctypes.byref(h)))
+        self._h = h
+        self.n_layers = n_layers
+
+    def close(self) -> None:
+        if self._h:
+            self._lib.pa_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def submit(self, prompt_tokens: int, max_new_tokens: int) -> Optional[int]:
+        """The request id, or None when its budget exceeds the whole pool (rejected)."""
+        rid = ctypes.c_int64()
+        st = self._lib.pa_sched_submit(self._h, prompt_tokens, max_new_tokens, ctypes.byref(rid))
+        if st == -7:
+            return None
+        _check("pa_sched_submit", st)
+        return rid.value
+
+    def admit(self, capacity: int = 1 << 16):
+        ids = (ctypes.c_int64 * max(capacity, 1))()
+        n = ctypes.c_int32()
+        _check("pa_sched_admit", self._lib.pa_sched_admit(self._h, ids, capacity, ctypes.byref(n)))
+        return [ids[i] for i in range(n.value)]
+
+    def grow(self, rid: int, new_length: int) -> bool:
+        """False when new_length is beyond the request's budget (nothing assigned)."""
+        st = self._lib.pa_sched_grow(self._h, rid, new_length)
+        if st == -8:
+            return False
+        _check("pa_sched_grow", st)
+        return True
+
+    def block_table(self, rid: int, layer: int, max_blocks: int):
+        import numpy as np
+        row = np.empty(max_blocks, np.int32)
+        _check("pa_sched_block_table", self._lib.pa_sched_block_table(
+            self._h, rid, layer, row.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), max_blocks))
+        return row
+
+    def finish(self, rid: int) -> None:
+        _check("pa_sched_finish", self._lib.pa_sched_finish(self._h, rid))
+
+    def decode_batch(self, n: int) -> None:
+        _check("pa_sched_decode_batch", self._lib.pa_sched_decode_batch(self._h, n))
+
+    def stats(self) -> dict:
+        st = SchedStats()
+        _check("pa_sched_get_stats", self._lib.pa_sched_get_stats(self._h, ctypes.byref(st)))
+        return {name: getattr(st, name) for name, _ in SchedStats._fields_}
