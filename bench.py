@@ -47,7 +47,7 @@ FILL_METRIC = "prefill page fill: effective GB/s (K/V rows read + written), µs/
 
 def measured_traffic(profile=None):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
-    taken on the current kernel source (pa_kernels.hip, pa_api.cpp); else None."""
+    taken on the current kernel source (pa_kernels.hip, pa_kernels.h); else None."""
     import hashlib
     import re
     try:
@@ -59,7 +59,7 @@ def measured_traffic(profile=None):
     if not (m_sha and m_tr):
         return None
     h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_api.cpp"):
+    for f in ("pa_kernels.hip", "pa_kernels.h"):
         with open(os.path.join(ROOT, "paged_kv_cache_205_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return int(m_tr.group(1)) if h.hexdigest() == m_sha.group(1) else None
@@ -190,6 +190,34 @@ def bench_fill(args, lay):
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def stream_read_reference(torch, dev, gib: int = 4, reps: int = 5):
+    """GB/s of a plain non-temporal streaming read of a 4 GiB buffer (libpa_probe.so), or None."""
+    import ctypes
+    path = os.path.join(ROOT, "paged_kv_cache_205_amd", "libpa_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.pa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_probe_stream_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    if lib.pa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), st) != 0:
+        return None
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        lib.pa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), st)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = reps * nbytes / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del buf
+    return gbs
 
 
 # ----------------------------------------------------------------------------
@@ -389,6 +417,8 @@ def main():
         except Exception as e:  # report, keep the stream number
             log(f"graph capture failed: {e!r}")
 
+    stream_gbs = stream_read_reference(torch, dev)
+
     kv_step = lay.kv_bytes_per_step
     best_ms = ms_step if graph_ms is None else min(ms_step, graph_ms)
     value = kv_step / (best_ms * 1e-3) / 1e9
@@ -427,6 +457,8 @@ def main():
         "us_per_step_separate_append_decode": round(ms_step_sep * 1e3, 2),
         "seq_steps_per_s": round(lay.B / (best_ms * 1e-3), 1),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "stream_read_GBps": None if stream_gbs is None else round(stream_gbs, 1),
+        "frac_stream_read": None if stream_gbs is None else round(value / stream_gbs, 4),
         "roofline": {
             "kernel": "decode_kernel<fused append> (one launch per layer: append, attention, split merge)",
             "bound": "hbm",

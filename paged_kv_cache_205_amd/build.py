@@ -38,6 +38,13 @@ def build(verbose: bool = False) -> str:
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
     os.replace(tmp, LIB)
+    # the streaming-read reference the benchmark times beside the kernels
+    probe = os.path.join(PKG, "libpa_probe.so")
+    cmd = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, "stream_probe.hip"), "-o", probe + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the streaming-read probe ({res.returncode}):\n{res.stderr}")
+    os.replace(probe + ".tmp", probe)
     return LIB
 
 
