@@ -24,6 +24,12 @@ Sources (web pages describing the samir-vllm teaching engine):
 * Prefill fill: prefill writes the K and V rows of a sequence's prompt tokens
   into that sequence's pages, through the same block table ([README] KV page
   pool item: prefill fills prompt pages).
+* Prefill attention: dense causal grouped-query attention over a prompt's own
+  contiguous K and V ([README] feature list: dense causal prefill runs
+  grouped-query attention in all 16 layers): position i of a prompt attends
+  positions 0..i,
+
+      out[i, h] = sum_{j <= i} softmax_j(scale * q[i, h] . k[j, g]) * v[j, g].
 * Decode attention: every query head reads its sequence's cached pages directly
   (no contiguous gather) and forms softmax-weighted sums of V ([README] paged
   decode attention item; [NF]).  The pages compute it with an FP32 online
@@ -118,6 +124,34 @@ def fill_ref(k_pool: np.ndarray, v_pool: np.ndarray, k_src: np.ndarray, v_src: n
             k_out[page, slot] = k_src[cu[b] + i]
             v_out[page, slot] = v_src[cu[b] + i]
     return k_out, v_out
+
+
+def prefill_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_tokens, scale: float) -> np.ndarray:
+    """Causal attention of each prompt over its own tokens, in FP64.
+
+    q: uint16 [T][Hq][D]; k, v: uint16 [T][Hkv][D] (BF16 bits), prompts one after
+    another: prompt b is rows cu_tokens[b] .. cu_tokens[b+1]-1.  Returns
+    float64 [T][Hq][D].  Query head h uses KV head h // (Hq / Hkv).
+    """
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((T, Hq, D))
+    cu = np.asarray(cu_tokens, dtype=np.int64)
+    for b in range(len(cu) - 1):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        n = r1 - r0
+        if n == 0:
+            continue
+        Q, K, V = bf16_to_f64(q[r0:r1]), bf16_to_f64(k[r0:r1]), bf16_to_f64(v[r0:r1])
+        later = np.triu(np.ones((n, n), dtype=bool), 1)  # j > i: not attended
+        for h in range(Hq):
+            g = h // G
+            s = scale * (Q[:, h] @ K[:, g].T)
+            s[later] = -np.inf
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            out[r0:r1, h] = (w @ V[:, g]) / w.sum(axis=1, keepdims=True)
+    return out
 
 
 def _walk(k_pool, v_pool, block_table_row, L, g, t0=0, t1=None):
