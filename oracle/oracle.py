@@ -154,6 +154,28 @@ def prefill_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_tokens, scale: f
     return out
 
 
+def prefill_rows_ref(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, starts, rows, scale: float) -> np.ndarray:
+    """Selected rows of the causal prefill attention, in FP64, one at a time.
+
+    q_rows: uint16 [R][Hq][D], the queries of packed rows ``rows``; k, v: uint16
+    [T][Hkv][D] (all prompts); starts[r]: first row of the prompt that rows[r]
+    belongs to.  Row r attends keys starts[r] .. rows[r], as in prefill_ref.
+    Returns float64 [R][Hq][D].
+    """
+    R, Hq, D = q_rows.shape
+    G = Hq // k.shape[1]
+    out = np.zeros((R, Hq, D))
+    for r in range(R):
+        j0, j1 = int(starts[r]), int(rows[r]) + 1
+        K, V = bf16_to_f64(k[j0:j1]), bf16_to_f64(v[j0:j1])
+        Q = bf16_to_f64(q_rows[r])
+        for h in range(Hq):
+            s = scale * (K[:, h // G] @ Q[h])
+            w = np.exp(s - s.max())
+            out[r, h] = (w @ V[:, h // G]) / w.sum()
+    return out
+
+
 def _walk(k_pool, v_pool, block_table_row, L, g, t0=0, t1=None):
     """Yield (K rows, V rows) as FP64 arrays for the tokens [t0, t1) of one sequence, page by page."""
     t1 = L if t1 is None else t1

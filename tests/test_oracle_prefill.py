@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 import scipy.special
 
-from oracle import bf16_to_f64, decode_ref, prefill_ref
+from oracle import bf16_to_f64, decode_ref, prefill_ref, prefill_rows_ref
 from tests.test_oracle import PT, rand_bits, to_bits
 
 
@@ -101,6 +101,20 @@ def test_gqa_isolation():
     v2[:, 1] = 0x7FC0
     got = prefill_ref(q, k2, v2, cu, 0.125)
     assert np.array_equal(got[:, :4], base[:, :4]) and np.isnan(got[:, 4:]).all()
+
+
+def test_rows_ref_equals_prefill_ref_row_by_row():
+    # prefill_rows_ref (one row at a time, for sampled rows of large inputs) gives
+    # the rows of the pinned prefill_ref, prompt boundaries included
+    q, k, v, cu = case(7, [1, 16, 0, 33, 9], sigma_k=2.0)
+    full = prefill_ref(q, k, v, cu, 0.3)
+    T = int(cu[-1])
+    rows = np.arange(T)
+    starts = cu[np.searchsorted(cu, rows, side="right") - 1]
+    got = prefill_rows_ref(q, k, v, starts, rows, 0.3)
+    assert np.allclose(got, full, rtol=1e-13, atol=1e-14)
+    pick = np.array([0, 1, 16, 17, 50, T - 1])
+    assert np.array_equal(prefill_rows_ref(q[pick], k, v, starts[pick], pick, 0.3), got[pick])
 
 
 # ---------------------------------------------------------------- planted slips
