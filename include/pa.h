@@ -66,6 +66,8 @@ extern "C" {
 #define PA_MAX_BLOCKS_LIMIT 4096
 #define PA_MAX_DECODE_BATCH 4096
 #define PA_MAX_FILL_BATCH 4096
+#define PA_MAX_PREFILL_BATCH 4096
+#define PA_MAX_PREFILL_ROWS (1 << 30)
 
 enum pa_status {
   PA_OK = 0,
@@ -128,6 +130,37 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
 int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint16_t* v_pool,
             const int32_t* block_table, int32_t max_blocks, const int32_t* start, const int32_t* cu_tokens,
             int32_t B, int64_t T, int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
+
+/*
+ * pa_prefill - dense causal attention of whole prompts over their own K and V,
+ * with grouped-query heads (prefill).  ([README] feature list: dense causal
+ * prefill, grouped-query attention in all layers; Llama 3.2 1B shapes, Hq = 32
+ * query heads sharing Hkv = 8 KV heads, D = 64.)
+ *
+ * Prompt b is rows cu_tokens[b] .. cu_tokens[b+1]-1; row i of it attends rows
+ * cu_tokens[b] .. i of the same prompt (the prompt's own positions up to i):
+ *
+ *   out[i][h][:] = sum_{j = cu_tokens[b]}^{i} softmax_j(scale * q[i][h] . k[j][g]) v[j][g],
+ *   g = h / (Hq / Hkv).
+ *
+ *   q            bf16 [T][Hq][D] (already position-encoded)
+ *   k, v         bf16 [T][Hkv][D], the prompts' own keys and values
+ *   cu_tokens    int32 [B+1] on the device: cu_tokens[0] = 0, nondecreasing,
+ *                cu_tokens[B] = T; empty prompts are allowed
+ *   out          fp32 [T][Hq][D] (written; every row of a prompt)
+ *   scale        softmax scale (1/sqrt(D) for the model)
+ *   B            1 .. PA_MAX_PREFILL_BATCH; T total rows, 0 .. PA_MAX_PREFILL_ROWS
+ * Arithmetic: scores and the online softmax in FP32; each weight enters the
+ * weighted sum of V as a bf16 pair (high part and remainder), about 2^-16
+ * relative.  Inputs are expected finite: a non-finite value in one prompt's V
+ * can reach rows of a neighbouring prompt that share its 16-row group.
+ * cu_tokens breaking the rules above gives unspecified output but no access
+ * outside q, k, v, out and cu_tokens[0 .. B].
+ * Returns PA_OK, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_NULL, PA_ERR_ALIGN
+ * or PA_ERR_LAUNCH; nothing is launched for T == 0.
+ */
+int pa_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu_tokens, int32_t B,
+               int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float scale, float* out, hipStream_t stream);
 
 /*
  * Bytes of workspace pa_decode and pa_append_decode need for these sizes

@@ -148,6 +148,28 @@ int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint
   return PA_OK;
 }
 
+int pa_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu_tokens, int32_t B,
+               int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float scale, float* out, hipStream_t stream) {
+  if (B <= 0 || B > PA_MAX_PREFILL_BATCH || T < 0 || T > PA_MAX_PREFILL_ROWS) return PA_ERR_SHAPE;
+  const int dims = check_dims(Hq, Hkv, D);
+  if (dims != PA_OK) return dims;
+  if (!isfinite(scale)) return PA_ERR_SHAPE;
+  if (T == 0) return PA_OK;
+  if (!q || !k || !v || !cu_tokens || !out) return PA_ERR_NULL;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out)) return PA_ERR_ALIGN;
+  pa::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_tokens = cu_tokens;
+  a.B = B;
+  a.T = (int)T;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.out = out;
+  if (pa::launch_prefill(a, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
                                  int32_t partition_tokens) {
   if (B <= 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return 0;

@@ -1,0 +1,285 @@
+// Dense causal prefill attention with grouped-query heads (pa_prefill).
+//
+// Source: the pages' feature list ([README], "6 Hours of YouTube and 85
+// handtyped pages of notes on LLM Inference - Start here"): dense causal
+// prefill runs grouped-query attention in all 16 layers over the prompt's own
+// K and V.  Position i of a prompt attends positions 0..i:
+//   out[i][h] = sum_{j <= i} softmax_j(scale * q[i][h] . k[j][g]) v[j][g],  g = h / 4.
+//
+// Work: one workgroup of 4 waves per (64 query positions, KV head g).  Wave w
+// owns positions r0 + 16w .. r0 + 16w + 15 for the 4 query heads of g, so each
+// K/V tile staged in LDS serves 16 query rows x 4 heads per wave.  Per tile of
+// 32 keys, for each head:
+//   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, A = K (16 keys x 32 dims from
+//                      LDS), B = Q^T (registers); lane (t, c) gets keys
+//                      4c..4c+3 (and 16 + 4c..) of query t;
+//   O^T += V^T P^T     v_mfma_f32_16x16x32_bf16, B = P^T: the lane's 8 weights,
+//                      in the order its scores arrived (keys 4c.., 16+4c..), so P
+//                      needs no shuffle; A = V^T read in the same key order; the
+//                      weights go in as a bf16 high part plus a bf16 remainder,
+//                      two MFMAs, for about 2^-16 relative error per weight.
+// The softmax is the FP32 online one: a running maximum per (query, head),
+// common to the 4 lanes that hold the query, raised (with a rescale) only when
+// a tile exceeds it; the row sums are kept per lane and added at the end.
+// Keys before the query's prompt or after the query are masked (the tile is
+// checked once per wave; only boundary tiles pay for the per-element mask).
+// K and V tiles are copied into LDS by the DMA path, two tiles in flight,
+// chunks of each 128-byte row XOR-swizzled so that the MFMA-layout reads are
+// free of bank conflicts.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kRows = 64;       // query positions per workgroup
+constexpr int kKeys = 32;       // keys per tile
+constexpr int kTileBytes = kKeys * 128;  // one plane of a tile: 32 keys x 64 dims x bf16
+constexpr int kStage = 2 * kTileBytes;   // K then V
+
+// Position of 16-byte chunk C of LDS key row `key`: C ^ swz(key).
+__device__ __forceinline__ int swz(int key) { return (key & 7) ^ ((key >> 3) << 1); }
+
+// Key (within a 32-key tile) of element i of lane group c in the S^T result
+// registers of the two 16-key halves, which is also MFMA k index 8c + i of O^T.
+__device__ __forceinline__ constexpr int key_of(int c, int i) { return i < 4 ? 4 * c + i : 16 + 4 * c + (i - 4); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for LDS data only (not for outstanding global loads or copies).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Start of the prompt that packed row r belongs to: cu[b] for the largest b with cu[b] <= r.
+__device__ __forceinline__ int prompt_start(const int32_t* cu, int B, int r) {
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= r) lo = mid; else hi = mid;
+  }
+  return cu[lo];
+}
+
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [2 stages][K, V][32 keys][128 B]
+  // Workgroup i takes KV head i % 8, so that the workgroups one XCD runs (every
+  // eighth) share one head's K and V in that XCD's L2; the latest row blocks,
+  // which have the most keys, start first.
+  const int g = blockIdx.x & 7;
+  const int nqb = gridDim.x >> 3;
+  const int r0 = (nqb - 1 - (int)(blockIdx.x >> 3)) * kRows;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, t = lane & 15, c = lane >> 4;
+  const int T = a.T;
+
+  // The lane's query row and its prompt's first row, kept in [0, r] so that
+  // every address below stays inside the inputs whatever cu_tokens holds.
+  const int r = r0 + 16 * w + t;
+  const bool row_ok = r < T;
+  const int s_r = row_ok ? min(max(prompt_start(a.cu_tokens, a.B, r), 0), r) : T;
+  // keys the workgroup reads: from its first row's prompt start to its last row
+  const int k_lo = __builtin_amdgcn_readfirstlane(min(max(prompt_start(a.cu_tokens, a.B, r0), 0), r0));
+  const int k_hi = min(r0 + kRows, T) - 1;
+  const int ntiles = (k_hi - k_lo) / kKeys + 1;
+  // The wave's rows: the first, the last one that exists, the earliest and the
+  // latest prompt start among them.
+  const int w_first = r0 + 16 * w;
+  const int w_last = min(w_first + 15, T - 1);
+  const bool w_rows = w_first < T;
+  const int s_min = __builtin_amdgcn_readfirstlane(s_r);  // lane 0 holds row w_first
+  int s_max = s_r;
+  s_max = max(s_max, __shfl_xor(s_max, 1));
+  s_max = max(s_max, __shfl_xor(s_max, 2));
+  s_max = max(s_max, __shfl_xor(s_max, 4));
+  s_max = max(s_max, __shfl_xor(s_max, 8));
+  s_max = __builtin_amdgcn_readfirstlane(s_max);
+
+  // Q^T operands: query row r, head 4g + h, dims 8c..8c+7 and 32 + 8c..
+  bf16x8 qb[4][2];
+  {
+    const uint16_t* qrow = a.q + ((size_t)(row_ok ? r : 0) * kQHeads + g * kGroup) * kHeadDim;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      qb[h][0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 8 * c));
+      qb[h][1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 32 + 8 * c));
+    }
+  }
+
+  // DMA: wave w copies keys 8w..8w+7 of a tile (lane: key 8w + lane/8, LDS
+  // position lane%8, which holds chunk (lane%8) ^ swz(key)); keys past the last
+  // row are read from the last row (and masked).
+  const int dkey = 8 * w + (lane >> 3);
+  const int dchunk = (lane & 7) ^ swz(dkey);
+  auto issue = [&](int stage, int j0) {
+    const int row = min(j0 + dkey, T - 1);
+    const size_t off = ((size_t)row * kKvHeads + g) * kHeadDim + 8 * dchunk;
+    unsigned char* dst = lds + stage * kStage + w * 1024;
+    __builtin_amdgcn_global_load_lds(a.k + off, dst, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(a.v + off, dst + kTileBytes, 16, 0, 2);
+  };
+
+  // LDS read offsets.  K (A of S^T): key 16*sub + t, dims 8c.. (chunk c) and 32 + 8c.. (chunk 4 + c).
+  int kofs[2][2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const int key = 16 * sub + t;
+    kofs[sub][0] = key * 128 + 16 * (c ^ swz(key));
+    kofs[sub][1] = key * 128 + 16 * ((4 + c) ^ swz(key));
+  }
+  // V^T (A of O^T): dim 16*dt + t; MFMA k index 8c + i is key key_of(c, i).
+  // Dim d sits in chunk 2dt + t/8, at position (2dt + t/8) ^ swz(key) =
+  // 2dt ^ (t/8 ^ swz(key)); the other address bits hold no part of 32dt, so
+  // the byte offset is vofs[i] ^ 32dt.
+  int vofs[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int key = key_of(c, i);
+    vofs[i] = kTileBytes + key * 128 + 16 * ((t >> 3) ^ swz(key)) + 2 * (t & 7);
+  }
+
+  f32x4 acc[4][4];  // [head][d tile]: O^T rows 16dt + 4c .. +3, query t
+#pragma unroll
+  for (int h = 0; h < 4; ++h)
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) acc[h][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+  }
+
+  issue(0, k_lo);
+  for (int it = 0; it < ntiles; ++it) {
+    const int j0 = k_lo + it * kKeys;
+    if (it + 1 < ntiles) {
+      issue((it + 1) & 1, j0 + kKeys);
+      wait_vmcnt<2>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();  // every wave's copies of this tile have landed
+    // the wave skips tiles none of its rows attend
+    if (w_rows && j0 <= w_last && j0 + kKeys > s_min) {
+      const unsigned char* st = lds + (it & 1) * kStage;
+      u32x4 kreg[2][2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        kreg[sub][0] = *reinterpret_cast<const u32x4*>(st + kofs[sub][0]);
+        kreg[sub][1] = *reinterpret_cast<const u32x4*>(st + kofs[sub][1]);
+      }
+      s16x8 vt[4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int o = vofs[i];
+        asm volatile("" : "+v"(o));  // keep 8 offsets live, not 32
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vt[dt][i] = *reinterpret_cast<const short*>(st + (o ^ (32 * dt)));
+      }
+
+      // every key of the tile visible to every row of the wave: no masking
+      const bool full = j0 >= s_max && j0 + kKeys - 1 <= w_first;
+      if (!full) {
+        // A key no row of the wave attends gets V = 0, so its zero weight adds an
+        // exact zero whatever the row it was read from holds.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = j0 + key_of(c, i);
+          const bool none = key > w_last || key < s_min;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) vt[dt][i] = none ? (short)0 : vt[dt][i];
+        }
+      }
+
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][0]), qb[h][0], s0, 0, 0, 0);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][1]), qb[h][1], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][0]), qb[h][0], s1, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][1]), qb[h][1], s1, 0, 0, 0);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = s0[i] * a.scale_log2;
+          x[4 + i] = s1[i] * a.scale_log2;
+        }
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int key = j0 + key_of(c, i);
+            if (key > r || key < s_r) x[i] = -INFINITY;
+          }
+        }
+        float xm = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) xm = fmaxf(xm, x[i]);
+        if (__builtin_amdgcn_ballot_w64(xm > m[h]) != 0) {
+          // the tile maximum of each query over its 4 lanes, then rescale
+          float tm = fmaxf(xm, __shfl_xor(xm, 16));
+          tm = fmaxf(tm, __shfl_xor(tm, 32));
+          const float mn = fmaxf(m[h], tm);
+          const float alpha = (mn == m[h]) ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
+          m[h] = mn;
+          l[h] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) acc[h][dt] *= alpha;
+        }
+        float p[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m[h]);
+        l[h] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        // p = hi + lo: the bf16 truncation of p and the bf16 truncation of the rest
+        unsigned hi[8], lo[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          hi[i] = __builtin_bit_cast(unsigned, p[i]);
+          lo[i] = __builtin_bit_cast(unsigned, p[i] - __builtin_bit_cast(float, hi[i] & 0xffff0000u));
+        }
+        u32x4 phi, plo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          phi[i] = __builtin_amdgcn_perm(hi[2 * i + 1], hi[2 * i], 0x07060302u);
+          plo[i] = __builtin_amdgcn_perm(lo[2 * i + 1], lo[2 * i], 0x07060302u);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, vt[dt]);
+          acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, phi), acc[h][dt], 0, 0, 0);
+          acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, plo), acc[h][dt], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  }
+
+  if (!row_ok) return;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float lt = l[h] + __shfl_xor(l[h], 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.f / lt;
+    float* orow = a.out + ((size_t)r * kQHeads + g * kGroup + h) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c) = acc[h][dt] * inv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  const int nqb = (a.T + kRows - 1) / kRows;
+  hipLaunchKernelGGL(prefill_kernel, dim3(nqb * kKvHeads), dim3(256), 2 * kStage, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -20,7 +20,7 @@ PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN", -7: "PA_ERR_REJECTED",
           -8: "PA_ERR_BUDGET", -9: "PA_ERR_STATE"}
-EXPORTS = ("pa_status_string", "pa_append", "pa_fill", "pa_decode_workspace_bytes",
+EXPORTS = ("pa_status_string", "pa_append", "pa_fill", "pa_prefill", "pa_decode_workspace_bytes",
            "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_merge",
            "pa_sched_budget_pages", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_admit",
            "pa_sched_grow", "pa_sched_block_table", "pa_sched_finish", "pa_sched_decode_batch",
@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
     lib.pa_append.restype = ctypes.c_int
     lib.pa_fill.argtypes = [P, P, P, P, P, I32, P, P, I32, I64, I32, I32, I64, P]
     lib.pa_fill.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [P, P, P, P, I32, I64, I32, I32, I32, F32, P, P]
+    lib.pa_prefill.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = SZ
     lib.pa_default_partition_tokens.argtypes = []
@@ -133,6 +135,25 @@ def pa_fill(k_src, v_src, k_pool, v_pool, block_table, cu_tokens, start=None, st
                      _ptr(start, torch.int32, "start"), _ptr(cu_tokens, torch.int32, "cu_tokens"), B, T, Hkv, D,
                      k_pool.shape[0], _stream(k_pool.device, stream))
     _check("pa_fill", st)
+
+
+def pa_prefill(q, k, v, cu_tokens, scale: float, out=None, stream=None) -> torch.Tensor:
+    """Causal attention of each prompt over its own rows: q bf16 [T][32][64], k/v bf16 [T][8][64]
+    (prompts one after another), cu_tokens int32 [B+1] on the device -> out fp32 [T][32][64]."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = cu_tokens.shape[0] - 1
+    if k.shape[0] != T or v.shape != k.shape:
+        raise PAError("pa_prefill", -2, "q, k and v must have the same rows, k and v the same shape")
+    if out is None:
+        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+    elif tuple(out.shape) != (T, Hq, D):
+        raise PAError("pa_prefill", -2, f"out must be [{T}][{Hq}][{D}]")
+    lib = load()
+    st = lib.pa_prefill(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _ptr(cu_tokens, torch.int32, "cu_tokens"), B, T,
+                        Hq, Hkv, D, float(scale), _ptr(out, torch.float32, "out"), _stream(q.device, stream))
+    _check("pa_prefill", st)
+    return out
 
 
 def pa_decode_workspace_bytes(B: int, max_blocks: int, partition_tokens: int = 0, Hq: int = 32, D: int = 64) -> int:

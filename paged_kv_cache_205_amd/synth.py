@@ -54,6 +54,7 @@ ROW_ELEMS = HKV * HEAD_DIM  # bf16 elements in one token row of one plane
 _S_LENS, _S_ALLOC = 0, 1
 # torch streams
 _S_Q, _S_K, _S_V, _S_KNEW, _S_VNEW = 2, 3, 4, 5, 6
+_S_PQ = 7  # prefill queries
 
 
 def _np_rng(config_id: int, draw: int, stream: int) -> np.random.Generator:
@@ -333,6 +334,18 @@ def prefill_inputs(lay: Layout, layer: int, device="cpu", chunk_rows: int = 1 <<
     k_src = (torch.cat(ks) if ks else empty).view(T, HKV, HEAD_DIM)
     v_src = (torch.cat(vs) if vs else empty).view(T, HKV, HEAD_DIM)
     return k_src, v_src, torch.from_numpy(cu).to(dev)
+
+
+def prefill_queries(lay: Layout, layer: int, device="cpu", chunk_rows: int = 1 << 20) -> torch.Tensor:
+    """Queries of one layer's prompt rows, bf16 [T][32][64] in the row order of
+    ``prefill_inputs`` (T = sum of max(L_b - 1, 0)), N(0, sigma_q) values drawn in
+    chunks of ``chunk_rows`` rows, each chunk from its own seeded generator."""
+    dev = torch.device(device)
+    T = int(np.maximum(lay.seq_lens.astype(np.int64) - 1, 0).sum())
+    parts = [_randn_bf16((min(chunk_rows, T - start), HQ, HEAD_DIM), lay.sigma_q, dev,
+                         _torch_seed(lay.config_id, lay.draw, _S_PQ, (layer << 16) | c))
+             for c, start in enumerate(range(0, T, chunk_rows))]
+    return torch.cat(parts) if parts else torch.empty((0, HQ, HEAD_DIM), dtype=torch.bfloat16, device=dev)
 
 
 def layer_pages(lay: Layout, layer: int, device="cpu", chunk_rows: int = 1 << 22):

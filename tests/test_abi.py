@@ -210,3 +210,31 @@ def test_fill_validation(lib):
     assert _fill(lib, B=0) == 0
     assert _fill(lib, T=0) == 0
     assert _fill(lib, B=0, ks=None, cu=None) == 0
+
+
+def _prefill(lib, **kw):
+    args = dict(q=A, k=A, v=A, cu=A, B=4, T=100, Hq=32, Hkv=8, D=64, scale=0.125, out=A, stream=None)
+    args.update(kw)
+    return lib.pa_prefill(args["q"], args["k"], args["v"], args["cu"], args["B"], args["T"], args["Hq"], args["Hkv"],
+                          args["D"], args["scale"], args["out"], args["stream"])
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, B=0) == -2
+    assert _prefill(lib, B=-1) == -2
+    assert _prefill(lib, B=4097) == -2
+    assert _prefill(lib, T=-1) == -2
+    assert _prefill(lib, T=(1 << 30) + 1) == -2
+    assert _prefill(lib, Hq=30) == -2
+    assert _prefill(lib, Hq=16, Hkv=4) == -3
+    assert _prefill(lib, D=128) == -3
+    assert _prefill(lib, scale=float("inf")) == -2
+    assert _prefill(lib, scale=float("nan")) == -2
+    assert _prefill(lib, q=None) == -1
+    assert _prefill(lib, cu=None) == -1
+    assert _prefill(lib, out=None) == -1
+    assert _prefill(lib, k=MIS) == -6
+    assert _prefill(lib, out=MIS) == -6
+    # nothing to do: no launch
+    assert _prefill(lib, T=0) == 0
+    assert _prefill(lib, T=0, q=None, out=None) == 0
