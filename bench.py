@@ -17,6 +17,11 @@ bounded sample of the same workload.
 ``--op fill`` measures the prefill page fill instead: every layer's prompt rows
 (positions 0..L-2 of each sequence of the workload, packed one sequence after
 another) written into the pool with one ``pa_fill`` per layer.
+
+``--op prefill`` measures the causal prefill attention over the same prompts:
+one ``pa_prefill`` per layer (each prompt's rows attend its own earlier rows),
+reported in TFLOP/s of attention arithmetic (4 D flops per attended
+(query, key) pair and query head) against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -42,12 +47,16 @@ def log(*a):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_full_b64_l2048.md")
 FILL_PROFILE = os.path.join(ROOT, "profiles", "fill_kernel_full_b64_l2047.md")
+PREFILL_PROFILE = os.path.join(ROOT, "profiles", "prefill_kernel_full_b64_l2047.md")
+PREFILL_METRIC = ("prefill attention: TFLOP/s (causal GQA, 4*D flops per attended pair and query head), "
+                  "µs/step at batch 64×2047")
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 FILL_METRIC = "prefill page fill: effective GB/s (K/V rows read + written), µs/step at batch 64×2047"
 
 
-def measured_traffic(profile=None):
+def measured_traffic(profile=None, sources=("pa_kernels.hip", "pa_kernels.h")):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
-    taken on the current kernel source (pa_kernels.hip, pa_kernels.h); else None."""
+    taken on the current kernel source (the given csrc files); else None."""
     import hashlib
     import re
     try:
@@ -59,7 +68,7 @@ def measured_traffic(profile=None):
     if not (m_sha and m_tr):
         return None
     h = hashlib.sha256()
-    for f in ("pa_kernels.hip", "pa_kernels.h"):
+    for f in sources:
         with open(os.path.join(ROOT, "paged_kv_cache_205_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return int(m_tr.group(1)) if h.hexdigest() == m_sha.group(1) else None
@@ -192,6 +201,139 @@ def bench_fill(args, lay):
     print(json.dumps(res), flush=True)
 
 
+def _oracle_prefill(b):
+    """prefill_ref for prompt b of the prefill sample; returns its attention flops."""
+    from threadpoolctl import threadpool_limits
+    from oracle import prefill_ref
+    d = _CPU["prefill"]
+    c0, c1 = int(d["cu"][b]), int(d["cu"][b + 1])
+    with threadpool_limits(1):
+        prefill_ref(d["q"][c0:c1], d["k"][c0:c1], d["v"][c0:c1], np.array([0, c1 - c0], np.int32), d["scale"])
+    n = c1 - c0
+    return n * (n + 1) // 2 * 32 * 4 * 64
+
+
+def prefill_flops(cu: np.ndarray) -> int:
+    """Attention flops of one layer: 4 D per attended (query, key) pair, for each of the 32 query heads."""
+    n = np.diff(cu.astype(np.int64))
+    return int((n * (n + 1) // 2).sum()) * 32 * 4 * 64
+
+
+def cpu_baseline_prefill(lay, n_prompts: int, workers: int):
+    """Time the oracle's prefill attention on the first n_prompts prompts of layer 0, one prompt per task."""
+    import torch
+    from paged_kv_cache_205_amd import synth
+    torch.set_num_threads(1)
+    ks, vs, cu = synth.prefill_inputs(lay, 0, "cpu")
+    q = synth.prefill_queries(lay, 0, "cpu")
+    _CPU["prefill"] = dict(q=synth.bits(q), k=synth.bits(ks), v=synth.bits(vs), cu=cu.numpy(), scale=lay.scale)
+    del q, ks, vs
+    items = list(range(min(n_prompts, lay.B)))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        flops = sum(pool.map(_oracle_prefill, items, chunksize=1))
+    tw = time.perf_counter() - t0
+    return {
+        "value": round(flops / tw / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"layer 0, prompts 0..{items[-1]} of the same prefill ({len(items)} prompts of "
+                  f"{int(cu[1] - cu[0])} rows): prefill_ref (FP64 NumPy, one BLAS thread each) in "
+                  f"{workers} worker processes, {tw:.1f} s wall",
+        "seconds": round(tw, 2),
+    }
+
+
+def bench_prefill(args, lay):
+    """One step = one pa_prefill per layer over every prompt's rows."""
+    cpu = None
+    if not args.no_cpu:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"cpu baseline (prefill): oracle on {workers} workers ...")
+        cpu = cpu_baseline_prefill(lay, args.cpu_prompts, workers)
+        log(f"cpu baseline: {cpu['value']:.6f} TFLOP/s ({cpu['seconds']} s)")
+    import torch
+    from paged_kv_cache_205_amd import ops, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load()
+    dev = "cuda"
+    src = []
+    for l in range(lay.n_layers):
+        k, v, cu = synth.prefill_inputs(lay, l, dev)
+        src.append((synth.prefill_queries(lay, l, dev), k, v, cu))
+    T = int(src[0][0].shape[0])
+    outs = [torch.empty((T, 32, 64), dtype=torch.float32, device=dev) for _ in range(lay.n_layers)]
+    flops_launch = prefill_flops(src[0][3].cpu().numpy())
+    bytes_launch = T * (32 * 64 * 2 + 2 * 8 * 64 * 2 + 32 * 64 * 4)  # q, k, v read once, out written once
+    if args.calib_copy_mib:
+        a = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        torch.empty_like(a).copy_(a)
+        del a
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(lay.n_layers):
+            q, k, v, cu = src[l]
+            ops.pa_prefill(q, k, v, cu, lay.scale, out=outs[l])
+
+    for _ in range(args.warmup):
+        step()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    launch_ms = ms_step / lay.n_layers
+    tflops = flops_launch / (launch_ms * 1e-3) / 1e12
+    res = {
+        "metric": PREFILL_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"causal prefill attention of {lay.name}: B={lay.B} prompts of L-1 tokens, "
+                        f"{lay.n_layers} layers, 32 q / 8 kv heads, D=64, FP32 output",
+            "batch": lay.B,
+            "rows_per_layer": T,
+            "layers": lay.n_layers,
+            "flops_per_step": flops_launch * lay.n_layers,
+            "timing": "stream launches",
+            "parallelism": "single GPU",
+        },
+        "us_per_step": round(ms_step * 1e3, 2),
+        "roofline": {
+            "kernel": "prefill_kernel (one launch per layer)",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": (measured_traffic(PREFILL_PROFILE, ("pa_prefill.hip", "pa_kernels.h"))
+                        if lay.name == "full" else None),
+            "flops_per_launch": flops_launch,
+            "min_hbm_bytes_per_launch": bytes_launch,
+            "mean_launch_us": round(launch_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def stream_read_reference(torch, dev, gib: int = 4, reps: int = 5):
     """GB/s of a plain non-temporal streaming read of a 4 GiB buffer (libpa_probe.so), or None."""
     import ctypes
@@ -295,8 +437,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the workload the oracle runs on")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
-    ap.add_argument("--op", choices=("decode", "fill"), default="decode",
-                    help="decode: the decode step (default); fill: the prefill page fill")
+    ap.add_argument("--op", choices=("decode", "fill", "prefill"), default="decode",
+                    help="decode: the decode step (default); fill: the prefill page fill; "
+                         "prefill: the causal prefill attention")
+    ap.add_argument("--cpu-prompts", type=int, default=64, help="prompts of layer 0 the prefill oracle runs on")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -310,6 +454,9 @@ def main():
     lay = synth.get(args.config)
     if args.op == "fill":
         bench_fill(args, lay)
+        return
+    if args.op == "prefill":
+        bench_prefill(args, lay)
         return
 
     cpu = None

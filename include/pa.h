@@ -151,7 +151,7 @@ int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint
  *   scale        softmax scale (1/sqrt(D) for the model)
  *   B            1 .. PA_MAX_PREFILL_BATCH; T total rows, 0 .. PA_MAX_PREFILL_ROWS
  * Arithmetic: scores and the online softmax in FP32; each weight enters the
- * weighted sum of V as a bf16 pair (high part and remainder), about 2^-16
+ * weighted sum of V as a bf16 pair (high part and remainder), within 2^-16
  * relative.  Inputs are expected finite: a non-finite value in one prompt's V
  * can reach rows of a neighbouring prompt that share its 16-row group.
  * cu_tokens breaking the rules above gives unspecified output but no access

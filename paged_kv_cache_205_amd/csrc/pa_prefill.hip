@@ -17,10 +17,11 @@
 //                      in the order its scores arrived (keys 4c.., 16+4c..), so P
 //                      needs no shuffle; A = V^T read in the same key order; the
 //                      weights go in as a bf16 high part plus a bf16 remainder,
-//                      two MFMAs, for about 2^-16 relative error per weight.
+//                      two MFMAs, for at most 2^-16 relative error per weight.
 // The softmax is the FP32 online one: a running maximum per (query, head),
 // common to the 4 lanes that hold the query, raised (with a rescale) only when
-// a tile exceeds it; the row sums are kept per lane and added at the end.
+// a tile exceeds it by more than 2^8 (the weights stay below 2^8); the row sums
+// are kept per lane and added at the end.
 // Keys before the query's prompt or after the query are masked (the tile is
 // checked once per wave; only boundary tiles pay for the per-element mask).
 // K and V tiles are copied into LDS by the DMA path, two tiles in flight,
@@ -39,11 +40,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = 64;       // query positions per workgroup
 constexpr int kKeys = 32;       // keys per tile
 constexpr int kTileBytes = kKeys * 128;  // one plane of a tile: 32 keys x 64 dims x bf16
 constexpr int kStage = 2 * kTileBytes;   // K then V
+constexpr float kSlack = 8.f;            // lazy-maximum slack, base-2 logits
 
 // Position of 16-byte chunk C of LDS key row `key`: C ^ swz(key).
 __device__ __forceinline__ int swz(int key) { return (key & 7) ^ ((key >> 3) << 1); }
@@ -67,6 +71,120 @@ __device__ __forceinline__ int prompt_start(const int32_t* cu, int B, int r) {
     if (cu[mid] <= r) lo = mid; else hi = mid;
   }
   return cu[lo];
+}
+
+// Running state of one wave: O^T accumulators, per-(query, head) maximum and
+// per-lane partial row sums.
+struct WaveState {
+  f32x4 acc[4][4];  // [head][d tile]: O^T rows 16dt + 4c .. +3, query t
+  float m[4];       // running maximum (base 2), the same in the 4 lanes of a query
+  float l[4];       // this lane's share of the row sum
+};
+
+// One 32-key tile for the wave's 16 rows x 4 heads.  masked (wave-uniform):
+// some key of the tile is outside some row's range [s_r, r]; masked scores
+// become -inf, which the exponential turns into exact zeros (c2 > 0).
+__device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st, const int (&kofs)[2][2],
+                                          const int (&vofs)[8], const bf16x8 (&qb)[4][2], float c2, bool masked,
+                                          int j0, int c, int r, int s_r, int s_min, int w_last) {
+  u32x4 kreg[2][2];
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    kreg[sub][0] = *reinterpret_cast<const u32x4*>(st + kofs[sub][0]);
+    kreg[sub][1] = *reinterpret_cast<const u32x4*>(st + kofs[sub][1]);
+  }
+  s16x8 vt[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int o = vofs[i];
+    asm volatile("" : "+v"(o));  // keep 8 offsets live, not 32
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) vt[dt][i] = *reinterpret_cast<const short*>(st + (o ^ (32 * dt)));
+  }
+
+  // S^T = K Q^T for the 4 heads
+  float sv[4][8];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][0]), qb[h][0], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][0]), qb[h][0], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][1]), qb[h][1], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][1]), qb[h][1], s1, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[h][i] = s0[i];
+      sv[h][4 + i] = s1[i];
+    }
+  }
+
+  if (masked) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = j0 + key_of(c, i);
+      const bool keep = key <= r && key >= s_r;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) sv[h][i] = keep ? sv[h][i] : -INFINITY;
+      // A key no row of the wave attends gets V = 0, so its zero weight adds an
+      // exact zero whatever the row it was read from holds.
+      const bool none = key > w_last || key < s_min;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) vt[dt][i] = none ? (short)0 : vt[dt][i];
+    }
+  }
+
+  // the lanes' largest scaled scores (-inf where every key is masked)
+  float xm[4];
+  bool raise = false;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float x = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x = fmaxf(x, sv[h][i]);
+    xm[h] = x * c2;
+    raise |= xm[h] > ws.m[h] + kSlack;
+  }
+  // Lazy maximum: the running maximum moves only when a score exceeds it by
+  // more than kSlack (base 2), so weights stay below 2^kSlack in between.
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float tm = fmaxf(xm[h], __shfl_xor(xm[h], 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float mn = fmaxf(ws.m[h], tm);
+      const float alpha = (mn == ws.m[h]) ? 1.f : __builtin_amdgcn_exp2f(ws.m[h] - mn);
+      ws.m[h] = mn;
+      ws.l[h] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) ws.acc[h][dt] *= alpha;
+    }
+  }
+
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const float nm = ws.m[h] == -INFINITY ? 0.f : -ws.m[h];
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][i], c2, nm));
+    ws.l[h] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    // p = hi + lo: p rounded to bf16, and the rest (exact in FP32) rounded to
+    // bf16; hi + lo is within 2^-16 of p, relatively
+    u32x4 phi, plo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned hp = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p[2 * i], p[2 * i + 1]}, bf16x2));
+      const float r0 = p[2 * i] - __builtin_bit_cast(float, hp << 16);
+      const float r1 = p[2 * i + 1] - __builtin_bit_cast(float, hp & 0xffff0000u);
+      phi[i] = hp;
+      plo[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, vt[dt]);
+      ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, phi), ws.acc[h][dt], 0, 0, 0);
+      ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, plo), ws.acc[h][dt], 0, 0, 0);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
@@ -103,14 +221,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   s_max = max(s_max, __shfl_xor(s_max, 8));
   s_max = __builtin_amdgcn_readfirstlane(s_max);
 
-  // Q^T operands: query row r, head 4g + h, dims 8c..8c+7 and 32 + 8c..
+  // Q^T operands: query row r, head 4g + h, dims 8c..8c+7 and 32 + 8c..  For
+  // a negative scale the signs of q are flipped (exact) and |scale| is used; a
+  // scale below 1e-30 acts as 1e-30 (every weight is then exactly 1, as for 0).
+  const float c2 = fmaxf(fabsf(a.scale_log2), 1e-30f);
+  const unsigned qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
   bf16x8 qb[4][2];
   {
     const uint16_t* qrow = a.q + ((size_t)(row_ok ? r : 0) * kQHeads + g * kGroup) * kHeadDim;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      qb[h][0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 8 * c));
-      qb[h][1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 32 + 8 * c));
+      qb[h][0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 8 * c) ^ qsign);
+      qb[h][1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 32 + 8 * c) ^ qsign);
     }
   }
 
@@ -146,16 +268,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     vofs[i] = kTileBytes + key * 128 + 16 * ((t >> 3) ^ swz(key)) + 2 * (t & 7);
   }
 
-  f32x4 acc[4][4];  // [head][d tile]: O^T rows 16dt + 4c .. +3, query t
-#pragma unroll
-  for (int h = 0; h < 4; ++h)
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) acc[h][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], l[4];
+  WaveState ws;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) ws.acc[h][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    ws.m[h] = -INFINITY;
+    ws.l[h] = 0.f;
   }
 
   issue(0, k_lo);
@@ -171,93 +290,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // the wave skips tiles none of its rows attend
     if (w_rows && j0 <= w_last && j0 + kKeys > s_min) {
       const unsigned char* st = lds + (it & 1) * kStage;
-      u32x4 kreg[2][2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        kreg[sub][0] = *reinterpret_cast<const u32x4*>(st + kofs[sub][0]);
-        kreg[sub][1] = *reinterpret_cast<const u32x4*>(st + kofs[sub][1]);
-      }
-      s16x8 vt[4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int o = vofs[i];
-        asm volatile("" : "+v"(o));  // keep 8 offsets live, not 32
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) vt[dt][i] = *reinterpret_cast<const short*>(st + (o ^ (32 * dt)));
-      }
-
-      // every key of the tile visible to every row of the wave: no masking
-      const bool full = j0 >= s_max && j0 + kKeys - 1 <= w_first;
-      if (!full) {
-        // A key no row of the wave attends gets V = 0, so its zero weight adds an
-        // exact zero whatever the row it was read from holds.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int key = j0 + key_of(c, i);
-          const bool none = key > w_last || key < s_min;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) vt[dt][i] = none ? (short)0 : vt[dt][i];
-        }
-      }
-
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][0]), qb[h][0], s0, 0, 0, 0);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][1]), qb[h][1], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][0]), qb[h][0], s1, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][1]), qb[h][1], s1, 0, 0, 0);
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = s0[i] * a.scale_log2;
-          x[4 + i] = s1[i] * a.scale_log2;
-        }
-        if (!full) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int key = j0 + key_of(c, i);
-            if (key > r || key < s_r) x[i] = -INFINITY;
-          }
-        }
-        float xm = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) xm = fmaxf(xm, x[i]);
-        if (__builtin_amdgcn_ballot_w64(xm > m[h]) != 0) {
-          // the tile maximum of each query over its 4 lanes, then rescale
-          float tm = fmaxf(xm, __shfl_xor(xm, 16));
-          tm = fmaxf(tm, __shfl_xor(tm, 32));
-          const float mn = fmaxf(m[h], tm);
-          const float alpha = (mn == m[h]) ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
-          m[h] = mn;
-          l[h] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) acc[h][dt] *= alpha;
-        }
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) p[i] = (x[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[i] - m[h]);
-        l[h] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-        // p = hi + lo: the bf16 truncation of p and the bf16 truncation of the rest
-        unsigned hi[8], lo[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hi[i] = __builtin_bit_cast(unsigned, p[i]);
-          lo[i] = __builtin_bit_cast(unsigned, p[i] - __builtin_bit_cast(float, hi[i] & 0xffff0000u));
-        }
-        u32x4 phi, plo;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          phi[i] = __builtin_amdgcn_perm(hi[2 * i + 1], hi[2 * i], 0x07060302u);
-          plo[i] = __builtin_amdgcn_perm(lo[2 * i + 1], lo[2 * i], 0x07060302u);
-        }
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x8 av = __builtin_bit_cast(bf16x8, vt[dt]);
-          acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, phi), acc[h][dt], 0, 0, 0);
-          acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, plo), acc[h][dt], 0, 0, 0);
-        }
-      }
+      // masking unless every key of the tile is visible to every row of the wave
+      const bool masked = !(j0 >= s_max && j0 + kKeys - 1 <= w_first);
+      tile_step(ws, st, kofs, vofs, qb, c2, masked, j0, c, r, s_r, s_min, w_last);
     }
     lds_barrier();  // every wave is done with this stage before it is refilled
   }
@@ -265,12 +300,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   if (!row_ok) return;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    float lt = l[h] + __shfl_xor(l[h], 16);
+    float lt = ws.l[h] + __shfl_xor(ws.l[h], 16);
     lt += __shfl_xor(lt, 32);
     const float inv = 1.f / lt;
     float* orow = a.out + ((size_t)r * kQHeads + g * kGroup + h) * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c) = acc[h][dt] * inv;
+    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c) = ws.acc[h][dt] * inv;
   }
 }
 
