@@ -24,7 +24,8 @@
 // are kept per lane and added at the end.
 // Keys before the query's prompt or after the query are masked (the tile is
 // checked once per wave; only boundary tiles pay for the per-element mask).
-// K and V tiles are copied into LDS by the DMA path, two tiles in flight,
+// K and V tiles are copied into LDS by the DMA path (a ring of three stages,
+// two tiles in flight, one workgroup barrier per tile),
 // chunks of each 128-byte row XOR-swizzled so that the MFMA-layout reads are
 // free of bank conflicts.
 
@@ -40,6 +41,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -47,6 +49,7 @@ constexpr int kRows = 64;       // query positions per workgroup
 constexpr int kKeys = 32;       // keys per tile
 constexpr int kTileBytes = kKeys * 128;  // one plane of a tile: 32 keys x 64 dims x bf16
 constexpr int kStage = 2 * kTileBytes;   // K then V
+constexpr int kStages = 3;               // LDS ring
 constexpr float kSlack = 8.f;            // lazy-maximum slack, base-2 logits
 
 // Position of 16-byte chunk C of LDS key row `key`: C ^ swz(key).
@@ -85,7 +88,7 @@ struct WaveState {
 // some key of the tile is outside some row's range [s_r, r]; masked scores
 // become -inf, which the exponential turns into exact zeros (c2 > 0).
 __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st, const int (&kofs)[2][2],
-                                          const int (&vofs)[8], const bf16x8 (&qb)[4][2], float c2, bool masked,
+                                          const int (&vofs)[2], const bf16x8 (&qb)[4][2], float c2, bool masked,
                                           int j0, int c, int r, int s_r, int s_min, int w_last) {
   u32x4 kreg[2][2];
 #pragma unroll
@@ -93,13 +96,19 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
     kreg[sub][0] = *reinterpret_cast<const u32x4*>(st + kofs[sub][0]);
     kreg[sub][1] = *reinterpret_cast<const u32x4*>(st + kofs[sub][1]);
   }
-  s16x8 vt[4];
+  // V^T by transposing LDS reads: read x of d tile dt gives lane (t, c) the 4
+  // values V[key_of(c, 4x + k)][16dt + t], k = 0..3.  Issued as inline
+  // assembly: the builtin makes the compiler wait for every outstanding copy
+  // into LDS first, the next tiles' included.  LDS operations of one wave
+  // complete in order, so the compiler's own lgkmcnt waits stay sufficient;
+  // these results are waited for explicitly below.
+  s16x4 vr[4][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int o = vofs[i];
-    asm volatile("" : "+v"(o));  // keep 8 offsets live, not 32
+  for (int x = 0; x < 2; ++x) {
+    const unsigned base = (unsigned)(uintptr_t)st + (unsigned)vofs[x];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) vt[dt][i] = *reinterpret_cast<const short*>(st + (o ^ (32 * dt)));
+    for (int dt = 0; dt < 4; ++dt)
+      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[dt][x]) : "v"(base ^ (32u * dt)));
   }
 
   // S^T = K Q^T for the 4 heads
@@ -117,6 +126,18 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
       sv[h][4 + i] = s1[i];
     }
   }
+
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(vr[0][0]), "+v"(vr[0][1]), "+v"(vr[1][0]), "+v"(vr[1][1]), "+v"(vr[2][0]), "+v"(vr[2][1]),
+                 "+v"(vr[3][0]), "+v"(vr[3][1]));
+  s16x8 vt[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      vt[dt][k] = vr[dt][0][k];
+      vt[dt][4 + k] = vr[dt][1][k];
+    }
 
   if (masked) {
 #pragma unroll
@@ -188,7 +209,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
 }
 
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [2 stages][K, V][32 keys][128 B]
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [3 stages][K, V][32 keys][128 B]
   // Workgroup i takes KV head i % 8, so that the workgroups one XCD runs (every
   // eighth) share one head's K and V in that XCD's L2; the latest row blocks,
   // which have the most keys, start first.
@@ -234,6 +255,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       qb[h][0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 8 * c) ^ qsign);
       qb[h][1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + h * kHeadDim + 32 + 8 * c) ^ qsign);
     }
+    // take the queries in now, not behind the first tiles' copies
+    asm volatile("" : "+v"(qb[0][0]), "+v"(qb[0][1]), "+v"(qb[1][0]), "+v"(qb[1][1]), "+v"(qb[2][0]), "+v"(qb[2][1]),
+                 "+v"(qb[3][0]), "+v"(qb[3][1]));
   }
 
   // DMA: wave w copies keys 8w..8w+7 of a tile (lane: key 8w + lane/8, LDS
@@ -257,15 +281,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     kofs[sub][0] = key * 128 + 16 * (c ^ swz(key));
     kofs[sub][1] = key * 128 + 16 * ((4 + c) ^ swz(key));
   }
-  // V^T (A of O^T): dim 16*dt + t; MFMA k index 8c + i is key key_of(c, i).
-  // Dim d sits in chunk 2dt + t/8, at position (2dt + t/8) ^ swz(key) =
-  // 2dt ^ (t/8 ^ swz(key)); the other address bits hold no part of 32dt, so
-  // the byte offset is vofs[i] ^ 32dt.
-  int vofs[8];
+  // V^T (A of O^T) by transposing reads (ds_read_b64_tr_b16): in each group of
+  // 16 lanes (fixed c), lane t of read x supplies the address of the 4 dims
+  // 16dt + 4(t%4) .. +3 of key key_of(c, 4x + t/4) and receives dim 16dt + t of
+  // those 4 keys.  The dims sit in chunk 2dt + (t/2)%2, at position
+  // 2dt ^ ((t/2)%2 ^ swz(key)); the other address bits hold no part of 32dt,
+  // so the byte offset is vofs[x] ^ 32dt.
+  int vofs[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = key_of(c, i);
-    vofs[i] = kTileBytes + key * 128 + 16 * ((t >> 3) ^ swz(key)) + 2 * (t & 7);
+  for (int x = 0; x < 2; ++x) {
+    const int key = key_of(c, 4 * x + (t >> 2));
+    vofs[x] = kTileBytes + key * 128 + 16 * (((t >> 1) & 1) ^ swz(key)) + 8 * (t & 1);
   }
 
   WaveState ws;
@@ -277,24 +303,42 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     ws.l[h] = 0.f;
   }
 
+  // Three LDS stages, two tiles in flight: the one barrier per tile both
+  // publishes tile it and retires tile it - 1, whose stage then takes tile it + 2.
   issue(0, k_lo);
-  for (int it = 0; it < ntiles; ++it) {
-    const int j0 = k_lo + it * kKeys;
-    if (it + 1 < ntiles) {
-      issue((it + 1) & 1, j0 + kKeys);
-      wait_vmcnt<2>();
-    } else {
+  if (ntiles > 1) issue(1, k_lo + kKeys);
+  int cur = 0;  // stage of tile it
+  auto sync = [&](int it) {
+    if (it + 1 < ntiles)
+      wait_vmcnt<2>();  // this wave's copies of tile it have landed (tile it + 1's may not)
+    else
       wait_vmcnt<0>();
-    }
-    lds_barrier();  // every wave's copies of this tile have landed
-    // the wave skips tiles none of its rows attend
-    if (w_rows && j0 <= w_last && j0 + kKeys > s_min) {
-      const unsigned char* st = lds + (it & 1) * kStage;
-      // masking unless every key of the tile is visible to every row of the wave
-      const bool masked = !(j0 >= s_max && j0 + kKeys - 1 <= w_first);
-      tile_step(ws, st, kofs, vofs, qb, c2, masked, j0, c, r, s_r, s_min, w_last);
-    }
-    lds_barrier();  // every wave is done with this stage before it is refilled
+    lds_barrier();  // every wave's copies of tile it have landed; tile it - 1 is done
+    const int prev = cur == 0 ? 2 : cur - 1;  // stage of tile it - 1 = stage of tile it + 2
+    if (it + 2 < ntiles) issue(prev, k_lo + (it + 2) * kKeys);
+  };
+  auto advance = [&]() { cur = cur == 2 ? 0 : cur + 1; };
+  // The tiles some row of the wave attends: keys from s_min to w_last.  Every
+  // wave takes part in every tile's barrier; the loops are split so that the
+  // accumulators only live through the middle one.
+  const int t_lo = w_rows ? max(0, (s_min - k_lo) / kKeys) : ntiles;
+  const int t_hi = w_rows ? min(ntiles - 1, (w_last - k_lo) / kKeys) : ntiles - 1;
+  int it = 0;
+  for (; it < t_lo; ++it) {
+    sync(it);
+    advance();
+  }
+  for (; it <= t_hi; ++it) {
+    sync(it);
+    const int j0 = k_lo + it * kKeys;
+    // masking unless every key of the tile is visible to every row of the wave
+    const bool masked = !(j0 >= s_max && j0 + kKeys - 1 <= w_first);
+    tile_step(ws, lds + cur * kStage, kofs, vofs, qb, c2, masked, j0, c, r, s_r, s_min, w_last);
+    advance();
+  }
+  for (; it < ntiles; ++it) {
+    sync(it);
+    advance();
   }
 
   if (!row_ok) return;
@@ -313,7 +357,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int nqb = (a.T + kRows - 1) / kRows;
-  hipLaunchKernelGGL(prefill_kernel, dim3(nqb * kKvHeads), dim3(256), 2 * kStage, stream, a);
+  hipLaunchKernelGGL(prefill_kernel, dim3(nqb * kKvHeads), dim3(256), kStages * kStage, stream, a);
   return hipGetLastError();
 }
 
