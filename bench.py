@@ -47,7 +47,8 @@ def log(*a):
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_kernel_full_b64_l2048.md")
 FILL_PROFILE = os.path.join(ROOT, "profiles", "fill_kernel_full_b64_l2047.md")
-PREFILL_PROFILE = os.path.join(ROOT, "profiles", "prefill_kernel_full_b64_l2047.md")
+PREFILL_PROFILE = {"bf16x2": os.path.join(ROOT, "profiles", "prefill_kernel_full_b64_l2047.md"),
+                   "fp16": os.path.join(ROOT, "profiles", "prefill_kernel_fp16w_full_b64_l2047.md")}
 PREFILL_METRIC = ("prefill attention: TFLOP/s (causal GQA, 4*D flops per attended pair and query head), "
                   "µs/step at batch 64×2047")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -277,7 +278,7 @@ def bench_prefill(args, lay):
     def step():
         for l in range(lay.n_layers):
             q, k, v, cu = src[l]
-            ops.pa_prefill(q, k, v, cu, lay.scale, out=outs[l])
+            ops.pa_prefill(q, k, v, cu, lay.scale, out=outs[l], weights=args.prefill_weights)
 
     for _ in range(args.warmup):
         step()
@@ -312,18 +313,19 @@ def bench_prefill(args, lay):
             "rows_per_layer": T,
             "layers": lay.n_layers,
             "flops_per_step": flops_launch * lay.n_layers,
+            "weights": args.prefill_weights,
             "timing": "stream launches",
             "parallelism": "single GPU",
         },
         "us_per_step": round(ms_step * 1e3, 2),
         "roofline": {
-            "kernel": "prefill_kernel (one launch per layer)",
+            "kernel": f"prefill_kernel<{args.prefill_weights} weights> (one launch per layer)",
             "bound": "mfma",
             "achieved": round(tflops, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": (measured_traffic(PREFILL_PROFILE, ("pa_prefill.hip", "pa_kernels.h"))
+            "traffic": (measured_traffic(PREFILL_PROFILE[args.prefill_weights], ("pa_prefill.hip", "pa_kernels.h"))
                         if lay.name == "full" else None),
             "flops_per_launch": flops_launch,
             "min_hbm_bytes_per_launch": bytes_launch,
@@ -441,6 +443,8 @@ def main():
                     help="decode: the decode step (default); fill: the prefill page fill; "
                          "prefill: the causal prefill attention")
     ap.add_argument("--cpu-prompts", type=int, default=64, help="prompts of layer 0 the prefill oracle runs on")
+    ap.add_argument("--prefill-weights", choices=("bf16x2", "fp16"), default="bf16x2",
+                    help="prefill: weights as bf16 pairs (default) or fp16 weights with fp16 V")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     args = ap.parse_args()

@@ -68,6 +68,8 @@ extern "C" {
 #define PA_MAX_FILL_BATCH 4096
 #define PA_MAX_PREFILL_BATCH 4096
 #define PA_MAX_PREFILL_ROWS (1 << 30)
+#define PA_PREFILL_WEIGHTS_BF16X2 0
+#define PA_PREFILL_WEIGHTS_FP16 1
 
 enum pa_status {
   PA_OK = 0,
@@ -150,17 +152,24 @@ int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint
  *   out          fp32 [T][Hq][D] (written; every row of a prompt)
  *   scale        softmax scale (1/sqrt(D) for the model)
  *   B            1 .. PA_MAX_PREFILL_BATCH; T total rows, 0 .. PA_MAX_PREFILL_ROWS
- * Arithmetic: scores and the online softmax in FP32; each weight enters the
- * weighted sum of V as a bf16 pair (high part and remainder), within 2^-16
- * relative.  Inputs are expected finite: a non-finite value in one prompt's V
- * can reach rows of a neighbouring prompt that share its 16-row group.
+ *   weights      how the softmax weights meet V (scores, maxima and sums are FP32):
+ *     PA_PREFILL_WEIGHTS_BF16X2  each weight as a bf16 pair (high part and
+ *                remainder, within 2^-16 relative) times bf16 V: two MFMAs.
+ *     PA_PREFILL_WEIGHTS_FP16    each weight rounded to fp16 (2^-11), V converted
+ *                to fp16 (exact for |v| in [2^-17, 65504]; smaller values to
+ *                within 2^-25; larger ones overflow), the row sum taken over the
+ *                rounded weights: one MFMA; the error of an output is at most
+ *                about 2^-10 times the spread of the V values it averages.
+ * Inputs are expected finite: a non-finite value in one prompt's V can reach
+ * rows of a neighbouring prompt that share its 16-row group.
  * cu_tokens breaking the rules above gives unspecified output but no access
  * outside q, k, v, out and cu_tokens[0 .. B].
  * Returns PA_OK, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED, PA_ERR_NULL, PA_ERR_ALIGN
  * or PA_ERR_LAUNCH; nothing is launched for T == 0.
  */
 int pa_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu_tokens, int32_t B,
-               int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float scale, float* out, hipStream_t stream);
+               int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t weights, float* out,
+               hipStream_t stream);
 
 /*
  * Bytes of workspace pa_decode and pa_append_decode need for these sizes

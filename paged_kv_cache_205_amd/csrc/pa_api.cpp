@@ -149,8 +149,10 @@ int pa_fill(const uint16_t* k_src, const uint16_t* v_src, uint16_t* k_pool, uint
 }
 
 int pa_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const int32_t* cu_tokens, int32_t B,
-               int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float scale, float* out, hipStream_t stream) {
+               int64_t T, int32_t Hq, int32_t Hkv, int32_t D, float scale, int32_t weights, float* out,
+               hipStream_t stream) {
   if (B <= 0 || B > PA_MAX_PREFILL_BATCH || T < 0 || T > PA_MAX_PREFILL_ROWS) return PA_ERR_SHAPE;
+  if (weights != PA_PREFILL_WEIGHTS_BF16X2 && weights != PA_PREFILL_WEIGHTS_FP16) return PA_ERR_SHAPE;
   const int dims = check_dims(Hq, Hkv, D);
   if (dims != PA_OK) return dims;
   if (!isfinite(scale)) return PA_ERR_SHAPE;
@@ -165,6 +167,7 @@ int pa_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const in
   a.B = B;
   a.T = (int)T;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.fp16_weights = weights == PA_PREFILL_WEIGHTS_FP16;
   a.out = out;
   if (pa::launch_prefill(a, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;

@@ -82,6 +82,7 @@ struct PrefillArgs {
   int B;
   int T;
   float scale_log2;            // scale * log2(e)
+  int fp16_weights;            // 0: weights as a bf16 pair with bf16 V; 1: fp16 weights and fp16 V
   float* out;                  // [T][Hq][D]
 };
 

@@ -44,6 +44,8 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kRows = 64;       // query positions per workgroup
 constexpr int kKeys = 32;       // keys per tile
@@ -81,12 +83,14 @@ __device__ __forceinline__ int prompt_start(const int32_t* cu, int B, int r) {
 struct WaveState {
   f32x4 acc[4][4];  // [head][d tile]: O^T rows 16dt + 4c .. +3, query t
   float m[4];       // running maximum (base 2), the same in the 4 lanes of a query
-  float l[4];       // this lane's share of the row sum
+  float l[4];       // bf16-pair weights: this lane's share of the row sum
+  f32x4 lsum[4];    // fp16 weights: the row sum of the rounded weights (every register)
 };
 
 // One 32-key tile for the wave's 16 rows x 4 heads.  masked (wave-uniform):
 // some key of the tile is outside some row's range [s_r, r]; masked scores
 // become -inf, which the exponential turns into exact zeros (c2 > 0).
+template <bool kF16>
 __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st, const int (&kofs)[2][2],
                                           const int (&vofs)[2], const bf16x8 (&qb)[4][2], float c2, bool masked,
                                           int j0, int c, int r, int s_r, int s_min, int w_last) {
@@ -154,6 +158,18 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
     }
   }
 
+  if (kF16) {  // V in fp16: exact for the bf16 values within the fp16 range
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      u32x4 w = __builtin_bit_cast(u32x4, vt[dt]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = __builtin_bit_cast(unsigned, __builtin_convertvector(
+                   (f32x2){__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xffff0000u)}, f16x2));
+      vt[dt] = __builtin_bit_cast(s16x8, w);
+    }
+  }
+
   // the lanes' largest scaled scores (-inf where every key is masked)
   float xm[4];
   bool raise = false;
@@ -175,7 +191,10 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
       const float mn = fmaxf(ws.m[h], tm);
       const float alpha = (mn == ws.m[h]) ? 1.f : __builtin_amdgcn_exp2f(ws.m[h] - mn);
       ws.m[h] = mn;
-      ws.l[h] *= alpha;
+      if (kF16)
+        ws.lsum[h] *= alpha;
+      else
+        ws.l[h] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) ws.acc[h][dt] *= alpha;
     }
@@ -187,27 +206,43 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][i], c2, nm));
-    ws.l[h] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-    // p = hi + lo: p rounded to bf16, and the rest (exact in FP32) rounded to
-    // bf16; hi + lo is within 2^-16 of p, relatively
-    u32x4 phi, plo;
+    if (kF16) {
+      // p rounded to fp16 (2^-11 relative); the row sum is taken over the same
+      // rounded weights, by an MFMA against a tile of ones
+      u32x4 ph;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned hp = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p[2 * i], p[2 * i + 1]}, bf16x2));
-      const float r0 = p[2 * i] - __builtin_bit_cast(float, hp << 16);
-      const float r1 = p[2 * i + 1] - __builtin_bit_cast(float, hp & 0xffff0000u);
-      phi[i] = hp;
-      plo[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
-    }
+      for (int i = 0; i < 4; ++i)
+        ph[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p[2 * i], p[2 * i + 1]}, f16x2));
+      const f16x8 pb = __builtin_bit_cast(f16x8, ph);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, vt[dt]);
-      ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, phi), ws.acc[h][dt], 0, 0, 0);
-      ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, plo), ws.acc[h][dt], 0, 0, 0);
+      for (int dt = 0; dt < 4; ++dt)
+        ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vt[dt]), pb, ws.acc[h][dt], 0, 0, 0);
+      const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
+      ws.lsum[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb, ws.lsum[h], 0, 0, 0);
+    } else {
+      ws.l[h] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      // p = hi + lo: p rounded to bf16, and the rest (exact in FP32) rounded to
+      // bf16; hi + lo is within 2^-16 of p, relatively
+      u32x4 phi, plo;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned hp = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){p[2 * i], p[2 * i + 1]}, bf16x2));
+        const float r0 = p[2 * i] - __builtin_bit_cast(float, hp << 16);
+        const float r1 = p[2 * i + 1] - __builtin_bit_cast(float, hp & 0xffff0000u);
+        phi[i] = hp;
+        plo[i] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, vt[dt]);
+        ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, phi), ws.acc[h][dt], 0, 0, 0);
+        ws.acc[h][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8, plo), ws.acc[h][dt], 0, 0, 0);
+      }
     }
   }
 }
 
+template <bool kF16>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [3 stages][K, V][32 keys][128 B]
   // Workgroup i takes KV head i % 8, so that the workgroups one XCD runs (every
@@ -301,6 +336,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int dt = 0; dt < 4; ++dt) ws.acc[h][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.m[h] = -INFINITY;
     ws.l[h] = 0.f;
+    ws.lsum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // Three LDS stages, two tiles in flight: the one barrier per tile both
@@ -333,7 +369,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int j0 = k_lo + it * kKeys;
     // masking unless every key of the tile is visible to every row of the wave
     const bool masked = !(j0 >= s_max && j0 + kKeys - 1 <= w_first);
-    tile_step(ws, lds + cur * kStage, kofs, vofs, qb, c2, masked, j0, c, r, s_r, s_min, w_last);
+    tile_step<kF16>(ws, lds + cur * kStage, kofs, vofs, qb, c2, masked, j0, c, r, s_r, s_min, w_last);
     advance();
   }
   for (; it < ntiles; ++it) {
@@ -344,8 +380,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   if (!row_ok) return;
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    float lt = ws.l[h] + __shfl_xor(ws.l[h], 16);
-    lt += __shfl_xor(lt, 32);
+    float lt;
+    if (kF16) {
+      lt = ws.lsum[h][0];
+    } else {
+      lt = ws.l[h] + __shfl_xor(ws.l[h], 16);
+      lt += __shfl_xor(lt, 32);
+    }
     const float inv = 1.f / lt;
     float* orow = a.out + ((size_t)r * kQHeads + g * kGroup + h) * kHeadDim;
 #pragma unroll
@@ -357,7 +398,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   const int nqb = (a.T + kRows - 1) / kRows;
-  hipLaunchKernelGGL(prefill_kernel, dim3(nqb * kKvHeads), dim3(256), kStages * kStage, stream, a);
+  if (a.fp16_weights)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(nqb * kKvHeads), dim3(256), kStages * kStage, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(nqb * kKvHeads), dim3(256), kStages * kStage, stream, a);
   return hipGetLastError();
 }
 

@@ -50,7 +50,7 @@ def load() -> ctypes.CDLL:
     lib.pa_append.restype = ctypes.c_int
     lib.pa_fill.argtypes = [P, P, P, P, P, I32, P, P, I32, I64, I32, I32, I64, P]
     lib.pa_fill.restype = ctypes.c_int
-    lib.pa_prefill.argtypes = [P, P, P, P, I32, I64, I32, I32, I32, F32, P, P]
+    lib.pa_prefill.argtypes = [P, P, P, P, I32, I64, I32, I32, I32, F32, I32, P, P]
     lib.pa_prefill.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.pa_decode_workspace_bytes.restype = SZ
@@ -137,9 +137,15 @@ def pa_fill(k_src, v_src, k_pool, v_pool, block_table, cu_tokens, start=None, st
     _check("pa_fill", st)
 
 
-def pa_prefill(q, k, v, cu_tokens, scale: float, out=None, stream=None) -> torch.Tensor:
+PREFILL_WEIGHTS = {"bf16x2": 0, "fp16": 1}
+
+
+def pa_prefill(q, k, v, cu_tokens, scale: float, out=None, weights: str = "bf16x2", stream=None) -> torch.Tensor:
     """Causal attention of each prompt over its own rows: q bf16 [T][32][64], k/v bf16 [T][8][64]
-    (prompts one after another), cu_tokens int32 [B+1] on the device -> out fp32 [T][32][64]."""
+    (prompts one after another), cu_tokens int32 [B+1] on the device -> out fp32 [T][32][64].
+    weights: "bf16x2" (each weight as a bf16 pair, 2^-16) or "fp16" (fp16 weights and V, 2^-11)."""
+    if weights not in PREFILL_WEIGHTS:
+        raise ValueError(f"weights must be one of {sorted(PREFILL_WEIGHTS)}")
     T, Hq, D = q.shape
     Hkv = k.shape[1]
     B = cu_tokens.shape[0] - 1
@@ -151,7 +157,8 @@ def pa_prefill(q, k, v, cu_tokens, scale: float, out=None, stream=None) -> torch
         raise PAError("pa_prefill", -2, f"out must be [{T}][{Hq}][{D}]")
     lib = load()
     st = lib.pa_prefill(_bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _ptr(cu_tokens, torch.int32, "cu_tokens"), B, T,
-                        Hq, Hkv, D, float(scale), _ptr(out, torch.float32, "out"), _stream(q.device, stream))
+                        Hq, Hkv, D, float(scale), PREFILL_WEIGHTS[weights], _ptr(out, torch.float32, "out"),
+                        _stream(q.device, stream))
     _check("pa_prefill", st)
     return out
 

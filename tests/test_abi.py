@@ -213,10 +213,10 @@ def test_fill_validation(lib):
 
 
 def _prefill(lib, **kw):
-    args = dict(q=A, k=A, v=A, cu=A, B=4, T=100, Hq=32, Hkv=8, D=64, scale=0.125, out=A, stream=None)
+    args = dict(q=A, k=A, v=A, cu=A, B=4, T=100, Hq=32, Hkv=8, D=64, scale=0.125, weights=0, out=A, stream=None)
     args.update(kw)
     return lib.pa_prefill(args["q"], args["k"], args["v"], args["cu"], args["B"], args["T"], args["Hq"], args["Hkv"],
-                          args["D"], args["scale"], args["out"], args["stream"])
+                          args["D"], args["scale"], args["weights"], args["out"], args["stream"])
 
 
 def test_prefill_validation(lib):
@@ -230,6 +230,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, D=128) == -3
     assert _prefill(lib, scale=float("inf")) == -2
     assert _prefill(lib, scale=float("nan")) == -2
+    assert _prefill(lib, weights=2) == -2
+    assert _prefill(lib, weights=-1) == -2
     assert _prefill(lib, q=None) == -1
     assert _prefill(lib, cu=None) == -1
     assert _prefill(lib, out=None) == -1

@@ -38,11 +38,40 @@ def inputs(seed, lens, sigma_q=1.0, sigma_k=1.0):
     return (rand_bits(rng, (T, 32, 64), sigma_q), rand_bits(rng, (T, 8, 64), sigma_k), rand_bits(rng, (T, 8, 64)), cu)
 
 
-def run(q, k, v, cu, scale):
-    say(f"pa_prefill: B={len(cu) - 1} T={q.shape[0]} scale={scale}")
-    out = ops.pa_prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(cu).cuda(), scale)
+def run(q, k, v, cu, scale, weights="bf16x2"):
+    say(f"pa_prefill: B={len(cu) - 1} T={q.shape[0]} scale={scale} weights={weights}")
+    out = ops.pa_prefill(dev_bf16(q), dev_bf16(k), dev_bf16(v), torch.from_numpy(cu).cuda(), scale, weights=weights)
     torch.cuda.synchronize()
     return out.cpu().numpy()
+
+
+def v_spread(v: np.ndarray, cu: np.ndarray, rows=None) -> np.ndarray:
+    """max - min of V over the keys each row attends (its prompt up to itself), per KV head and dim,
+    expanded to the 32 query heads: [R][32][64]."""
+    V = bf16_to_f64(v)
+    hi = np.empty_like(V)
+    lo = np.empty_like(V)
+    for b in range(len(cu) - 1):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        hi[sl] = np.maximum.accumulate(V[sl], axis=0)
+        lo[sl] = np.minimum.accumulate(V[sl], axis=0)
+    spread = hi - lo if rows is None else hi[rows] - lo[rows]
+    return np.repeat(spread, 4, axis=1)
+
+
+def check_fp16_weights(got, ref, spread, what=""):
+    """fp16 weights (2^-11 each, the row sum over the same rounded weights) move an
+    output by at most 2^-10 times the spread of the V values it averages; 1e-5 more
+    for FP32 accumulation."""
+    got = np.asarray(got, dtype=np.float64)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bound = 2.0 ** -10 * spread + 1e-5
+    worst = float((err / bound).max()) if err.size else 0.0
+    say(f"{what}: fp16 weights, max abs {float(err.max()) if err.size else 0:.2e}, worst err/bound {worst:.3f}")
+    assert worst <= 1.0, f"{what}: error {worst:.3f} x the fp16-weight bound"
+    # on these N(0, 1) inputs the errors also stay inside the decode tolerance
+    check_close(got, ref, what)
 
 
 CASES = {
@@ -58,14 +87,18 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("weights", ["bf16x2", "fp16"])
 @pytest.mark.parametrize("name", list(CASES))
-def test_ragged_prompts(name):
+def test_ragged_prompts(name, weights):
     lens = CASES[name]
     q, k, v, cu = inputs(list(CASES).index(name), lens)
-    got = run(q, k, v, cu, 0.125)
+    got = run(q, k, v, cu, 0.125, weights)
     ref = prefill_ref(q, k, v, cu, 0.125)
-    mx = check_close(got, ref, name)
-    say(f"{name}: max abs {mx[0]:.2e}, row-rel {mx[1]:.2e}")
+    if weights == "fp16":
+        check_fp16_weights(got, ref, v_spread(v, cu), name)
+    else:
+        mx = check_close(got, ref, name)
+        say(f"{name}: max abs {mx[0]:.2e}, row-rel {mx[1]:.2e}")
 
 
 def test_full_length_prompt():
@@ -73,10 +106,15 @@ def test_full_length_prompt():
     check_close(run(q, k, v, cu, 0.125), prefill_ref(q, k, v, cu, 0.125), "2047-row prompt")
 
 
-@pytest.mark.parametrize("scale,sigma_k", [(0.0, 1.0), (0.125, 3.0), (1.0, 1.0), (4.0, 1.0)])
-def test_scales(scale, sigma_k):
+@pytest.mark.parametrize("weights", ["bf16x2", "fp16"])
+@pytest.mark.parametrize("scale,sigma_k", [(0.0, 1.0), (0.125, 3.0), (1.0, 1.0), (4.0, 1.0), (-0.5, 1.0)])
+def test_scales(scale, sigma_k, weights):
     q, k, v, cu = inputs(12, [77, 200, 9], sigma_k=sigma_k)
-    check_close(run(q, k, v, cu, scale), prefill_ref(q, k, v, cu, scale), f"scale {scale} sigma_k {sigma_k}")
+    got, ref = run(q, k, v, cu, scale, weights), prefill_ref(q, k, v, cu, scale)
+    if weights == "fp16":
+        check_fp16_weights(got, ref, v_spread(v, cu), f"scale {scale} sigma_k {sigma_k}")
+    else:
+        check_close(got, ref, f"scale {scale} sigma_k {sigma_k}")
 
 
 def test_scale_zero_gives_running_means():
@@ -87,10 +125,11 @@ def test_scale_zero_gives_running_means():
     check_close(got, np.repeat(means, 4, axis=1), "running means")
 
 
-def test_first_row_of_each_prompt_is_its_v_row():
+@pytest.mark.parametrize("weights", ["bf16x2", "fp16"])
+def test_first_row_of_each_prompt_is_its_v_row(weights):
     lens = [1, 16, 17, 40, 3]
     q, k, v, cu = inputs(14, lens)
-    got = run(q, k, v, cu, 0.125)
+    got = run(q, k, v, cu, 0.125, weights)
     for b in range(len(lens)):
         r = cu[b]
         for h in range(32):
@@ -137,7 +176,8 @@ def test_output_buffer_and_stream():
     check_close(out.cpu().numpy(), prefill_ref(q, k, v, cu, 0.125), "given out, side stream")
 
 
-def test_full_workload_sampled():
+@pytest.mark.parametrize("weights", ["bf16x2", "fp16"])
+def test_full_workload_sampled(weights):
     # the 64 x 2047-row prompt batch of the prefill benchmark (one layer): one
     # whole prompt against the full oracle, and sampled rows of every prompt
     lay = synth.full()
@@ -147,17 +187,24 @@ def test_full_workload_sampled():
     T = q.shape[0]
     assert T == 64 * 2047
     say(f"full workload: T={T}")
-    out = ops.pa_prefill(q, k, v, cu, lay.scale)
+    out = ops.pa_prefill(q, k, v, cu, lay.scale, weights=weights)
     torch.cuda.synchronize()
     cu_h = cu.cpu().numpy()
     qh, kh, vh = host_bits(q), host_bits(k), host_bits(v)
     got = out.cpu().numpy()
     b = 63
     sl = slice(int(cu_h[b]), int(cu_h[b + 1]))
-    check_close(got[sl], prefill_ref(qh[sl], kh[sl], vh[sl], np.array([0, 2047], np.int32), lay.scale),
-                "last prompt, every row")
+    one = np.array([0, 2047], np.int32)
+    ref = prefill_ref(qh[sl], kh[sl], vh[sl], one, lay.scale)
+    if weights == "fp16":
+        check_fp16_weights(got[sl], ref, v_spread(vh[sl], one), "last prompt, every row")
+    else:
+        check_close(got[sl], ref, "last prompt, every row")
     rng = np.random.default_rng(19)
     rows = np.concatenate([cu_h[:-1], cu_h[1:] - 1, rng.integers(0, T, 256)]).astype(np.int64)
     starts = cu_h[np.searchsorted(cu_h, rows, side="right") - 1]
     ref = prefill_rows_ref(qh[rows], kh, vh, starts, rows, lay.scale)
-    check_close(got[rows], ref, "sampled rows")
+    if weights == "fp16":
+        check_fp16_weights(got[rows], ref, v_spread(vh, cu_h, rows), "sampled rows")
+    else:
+        check_close(got[rows], ref, "sampled rows")
