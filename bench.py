@@ -202,11 +202,12 @@ def bench_fill(args, lay):
     print(json.dumps(res), flush=True)
 
 
-def _oracle_prefill(b):
-    """prefill_ref for prompt b of the prefill sample; returns its attention flops."""
+def _oracle_prefill(item):
+    """prefill_ref for one (layer, prompt) of the prefill sample; returns its attention flops."""
     from threadpoolctl import threadpool_limits
     from oracle import prefill_ref
-    d = _CPU["prefill"]
+    l, b = item
+    d = _CPU[("prefill", l)]
     c0, c1 = int(d["cu"][b]), int(d["cu"][b + 1])
     with threadpool_limits(1):
         prefill_ref(d["q"][c0:c1], d["k"][c0:c1], d["v"][c0:c1], np.array([0, c1 - c0], np.int32), d["scale"])
@@ -221,15 +222,18 @@ def prefill_flops(cu: np.ndarray) -> int:
 
 
 def cpu_baseline_prefill(lay, n_prompts: int, workers: int):
-    """Time the oracle's prefill attention on the first n_prompts prompts of layer 0, one prompt per task."""
+    """Time the oracle's prefill attention on the first n_prompts prompts (layer by layer), one prompt per task."""
     import torch
     from paged_kv_cache_205_amd import synth
     torch.set_num_threads(1)
-    ks, vs, cu = synth.prefill_inputs(lay, 0, "cpu")
-    q = synth.prefill_queries(lay, 0, "cpu")
-    _CPU["prefill"] = dict(q=synth.bits(q), k=synth.bits(ks), v=synth.bits(vs), cu=cu.numpy(), scale=lay.scale)
-    del q, ks, vs
-    items = list(range(min(n_prompts, lay.B)))
+    items = [(l, b) for l in range(lay.n_layers) for b in range(lay.B)][:max(1, n_prompts)]
+    for l in sorted({l for l, _ in items}):
+        ks, vs, cu = synth.prefill_inputs(lay, l, "cpu")
+        q = synth.prefill_queries(lay, l, "cpu")
+        _CPU[("prefill", l)] = dict(q=synth.bits(q), k=synth.bits(ks), v=synth.bits(vs), cu=cu.numpy(),
+                                    scale=lay.scale)
+        del q, ks, vs
+    rows = int(_CPU[("prefill", 0)]["cu"][1])
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(workers) as pool:
         flops = sum(pool.map(_oracle_prefill, items, chunksize=1))
@@ -239,9 +243,9 @@ def cpu_baseline_prefill(lay, n_prompts: int, workers: int):
         "unit": "TFLOP/s",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"layer 0, prompts 0..{items[-1]} of the same prefill ({len(items)} prompts of "
-                  f"{int(cu[1] - cu[0])} rows): prefill_ref (FP64 NumPy, one BLAS thread each) in "
-                  f"{workers} worker processes, {tw:.1f} s wall",
+        "sample": f"the first {len(items)} prompts ({rows} rows each; layers 0..{items[-1][0]}) of the same "
+                  f"prefill: prefill_ref (FP64 NumPy, one BLAS thread each) in {workers} worker processes, "
+                  f"{tw:.1f} s wall",
         "seconds": round(tw, 2),
     }
 
@@ -275,22 +279,28 @@ def bench_prefill(args, lay):
         del a
     torch.cuda.synchronize()
 
-    def step():
+    def step(weights):
         for l in range(lay.n_layers):
             q, k, v, cu = src[l]
-            ops.pa_prefill(q, k, v, cu, lay.scale, out=outs[l], weights=args.prefill_weights)
+            ops.pa_prefill(q, k, v, cu, lay.scale, out=outs[l], weights=weights)
 
-    for _ in range(args.warmup):
-        step()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for _ in range(args.steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
+
+    def timed(weights):
+        for _ in range(args.warmup):
+            step(weights)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            step(weights)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    ms_step = timed(args.prefill_weights)
+    other = "fp16" if args.prefill_weights == "bf16x2" else "bf16x2"
+    ms_other = timed(other)
     launch_ms = ms_step / lay.n_layers
     tflops = flops_launch / (launch_ms * 1e-3) / 1e12
     res = {
@@ -318,6 +328,12 @@ def bench_prefill(args, lay):
             "parallelism": "single GPU",
         },
         "us_per_step": round(ms_step * 1e3, 2),
+        "other_weights": {
+            "weights": other,
+            "value": round(flops_launch * lay.n_layers / (ms_other * 1e-3) / 1e12, 2),
+            "us_per_step": round(ms_other * 1e3, 2),
+            "frac_mfma_peak": round(flops_launch * lay.n_layers / (ms_other * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        },
         "roofline": {
             "kernel": f"prefill_kernel<{args.prefill_weights} weights> (one launch per layer)",
             "bound": "mfma",
@@ -442,7 +458,7 @@ def main():
     ap.add_argument("--op", choices=("decode", "fill", "prefill"), default="decode",
                     help="decode: the decode step (default); fill: the prefill page fill; "
                          "prefill: the causal prefill attention")
-    ap.add_argument("--cpu-prompts", type=int, default=64, help="prompts of layer 0 the prefill oracle runs on")
+    ap.add_argument("--cpu-prompts", type=int, default=192, help="prompts (layer by layer) the prefill oracle runs on")
     ap.add_argument("--prefill-weights", choices=("bf16x2", "fp16"), default="bf16x2",
                     help="prefill: weights as bf16 pairs (default) or fp16 weights with fp16 V")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

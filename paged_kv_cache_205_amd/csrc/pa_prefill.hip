@@ -304,8 +304,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int row = min(j0 + dkey, T - 1);
     const size_t off = ((size_t)row * kKvHeads + g) * kHeadDim + 8 * dchunk;
     unsigned char* dst = lds + stage * kStage + w * 1024;
-    __builtin_amdgcn_global_load_lds(a.k + off, dst, 16, 0, 2);
-    __builtin_amdgcn_global_load_lds(a.v + off, dst + kTileBytes, 16, 0, 2);
+    // cached loads: every row block of the prompt reads these rows again
+    __builtin_amdgcn_global_load_lds(a.k + off, dst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.v + off, dst + kTileBytes, 16, 0, 0);
   };
 
   // LDS read offsets.  K (A of S^T): key 16*sub + t, dims 8c.. (chunk c) and 32 + 8c.. (chunk 4 + c).
@@ -390,7 +391,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const float inv = 1.f / lt;
     float* orow = a.out + ((size_t)r * kQHeads + g * kGroup + h) * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c) = ws.acc[h][dt] * inv;
+    for (int dt = 0; dt < 4; ++dt)  // streaming stores: keep L2 for the keys and values
+      __builtin_nontemporal_store(ws.acc[h][dt] * inv, reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c));
   }
 }
 
