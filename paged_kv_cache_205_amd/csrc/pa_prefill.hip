@@ -24,10 +24,10 @@
 // are kept per lane and added at the end.
 // Keys before the query's prompt or after the query are masked (the tile is
 // checked once per wave; only boundary tiles pay for the per-element mask).
-// K and V tiles are copied into LDS by the DMA path (a ring of three stages,
-// two tiles in flight, one workgroup barrier per tile),
-// chunks of each 128-byte row XOR-swizzled so that the MFMA-layout reads are
-// free of bank conflicts.
+// K and V tiles are copied into LDS by the DMA path (a ring of four stages,
+// one workgroup barrier per tile), chunks of each 128-byte row XOR-swizzled so
+// that the MFMA-layout reads are free of bank conflicts.  The scores of tile
+// it + 1 are computed while tile it's weights are formed and applied.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,7 +51,7 @@ constexpr int kRows = 64;       // query positions per workgroup
 constexpr int kKeys = 32;       // keys per tile
 constexpr int kTileBytes = kKeys * 128;  // one plane of a tile: 32 keys x 64 dims x bf16
 constexpr int kStage = 2 * kTileBytes;   // K then V
-constexpr int kStages = 3;               // LDS ring
+constexpr int kStages = 4;               // LDS ring (a power of two)
 constexpr float kSlack = 8.f;            // lazy-maximum slack, base-2 logits
 
 // Position of 16-byte chunk C of LDS key row `key`: C ^ swz(key).
@@ -87,19 +87,53 @@ struct WaveState {
   f32x4 lsum[4];    // fp16 weights: the row sum of the rounded weights (every register)
 };
 
-// One 32-key tile for the wave's 16 rows x 4 heads.  masked (wave-uniform):
-// some key of the tile is outside some row's range [s_r, r]; masked scores
-// become -inf, which the exponential turns into exact zeros (c2 > 0).
-template <bool kF16>
-__device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st, const int (&kofs)[2][2],
-                                          const int (&vofs)[2], const bf16x8 (&qb)[4][2], float c2, bool masked,
-                                          int j0, int c, int r, int s_r, int s_min, int w_last) {
-  u32x4 kreg[2][2];
+// K tile operand (A of S^T): key 16*sub + t, dims 8c.. and 32 + 8c..
+__device__ __forceinline__ void load_k(u32x4 (&kreg)[2][2], const unsigned char* st, const int (&kofs)[2][2]) {
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     kreg[sub][0] = *reinterpret_cast<const u32x4*>(st + kofs[sub][0]);
     kreg[sub][1] = *reinterpret_cast<const u32x4*>(st + kofs[sub][1]);
   }
+}
+
+// Raw scores S^T = K Q^T of one tile for the 4 heads: sv[h][i] is key
+// key_of(c, i) of query t.
+__device__ __forceinline__ void scores(float (&sv)[4][8], const u32x4 (&kreg)[2][2], const bf16x8 (&qb)[4][2]) {
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][0]), qb[h][0], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][0]), qb[h][0], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][1]), qb[h][1], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][1]), qb[h][1], s1, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[h][i] = s0[i];
+      sv[h][4 + i] = s1[i];
+    }
+  }
+}
+
+// Per-tile geometry of the wave: first key, and whether some key of the tile is
+// outside some row's range [s_r, r] (wave-uniform).
+struct TileCtx {
+  int j0;
+  bool masked;
+};
+
+// Rows and ranges of the lane and the wave.
+struct RowCtx {
+  int c, r, s_r, s_min, w_last;
+};
+
+// Softmax and O^T += V^T P^T for tile `st` with scores sv, and, when kNext,
+// the scores of the next tile (K from st_next) into sn, whose MFMAs the
+// compiler can interleave with this tile's exponentials.  Masked scores become
+// -inf, which the exponential turns into exact zeros (c2 > 0).
+template <bool kF16, bool kNext>
+__device__ __forceinline__ void tile_step(WaveState& ws, float (&sv)[4][8], float (&sn)[4][8], const unsigned char* st,
+                                          const unsigned char* st_next, const int (&kofs)[2][2], const int (&vofs)[2],
+                                          const bf16x8 (&qb)[4][2], float c2, TileCtx tc, const RowCtx& rc) {
   // V^T by transposing LDS reads: read x of d tile dt gives lane (t, c) the 4
   // values V[key_of(c, 4x + k)][16dt + t], k = 0..3.  Issued as inline
   // assembly: the builtin makes the compiler wait for every outstanding copy
@@ -114,59 +148,16 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
     for (int dt = 0; dt < 4; ++dt)
       asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(vr[dt][x]) : "v"(base ^ (32u * dt)));
   }
+  u32x4 kn[2][2];
+  if (kNext) load_k(kn, st_next, kofs);
 
-  // S^T = K Q^T for the 4 heads
-  float sv[4][8];
-#pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][0]), qb[h][0], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][0]), qb[h][0], s1, 0, 0, 0);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[0][1]), qb[h][1], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[1][1]), qb[h][1], s1, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[h][i] = s0[i];
-      sv[h][4 + i] = s1[i];
-    }
-  }
-
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(vr[0][0]), "+v"(vr[0][1]), "+v"(vr[1][0]), "+v"(vr[1][1]), "+v"(vr[2][0]), "+v"(vr[2][1]),
-                 "+v"(vr[3][0]), "+v"(vr[3][1]));
-  s16x8 vt[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      vt[dt][k] = vr[dt][0][k];
-      vt[dt][4 + k] = vr[dt][1][k];
-    }
-
-  if (masked) {
+  if (tc.masked) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int key = j0 + key_of(c, i);
-      const bool keep = key <= r && key >= s_r;
+      const int key = tc.j0 + key_of(rc.c, i);
+      const bool keep = key <= rc.r && key >= rc.s_r;
 #pragma unroll
       for (int h = 0; h < 4; ++h) sv[h][i] = keep ? sv[h][i] : -INFINITY;
-      // A key no row of the wave attends gets V = 0, so its zero weight adds an
-      // exact zero whatever the row it was read from holds.
-      const bool none = key > w_last || key < s_min;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vt[dt][i] = none ? (short)0 : vt[dt][i];
-    }
-  }
-
-  if (kF16) {  // V in fp16: exact for the bf16 values within the fp16 range
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      u32x4 w = __builtin_bit_cast(u32x4, vt[dt]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = __builtin_bit_cast(unsigned, __builtin_convertvector(
-                   (f32x2){__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xffff0000u)}, f16x2));
-      vt[dt] = __builtin_bit_cast(s16x8, w);
     }
   }
 
@@ -199,6 +190,42 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
       for (int dt = 0; dt < 4; ++dt) ws.acc[h][dt] *= alpha;
     }
   }
+
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(vr[0][0]), "+v"(vr[0][1]), "+v"(vr[1][0]), "+v"(vr[1][1]), "+v"(vr[2][0]), "+v"(vr[2][1]),
+                 "+v"(vr[3][0]), "+v"(vr[3][1]));
+  s16x8 vt[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      vt[dt][k] = vr[dt][0][k];
+      vt[dt][4 + k] = vr[dt][1][k];
+    }
+  if (tc.masked) {
+    // A key no row of the wave attends gets V = 0, so its zero weight adds an
+    // exact zero whatever the row it was read from holds.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = tc.j0 + key_of(rc.c, i);
+      const bool none = key > rc.w_last || key < rc.s_min;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) vt[dt][i] = none ? (short)0 : vt[dt][i];
+    }
+  }
+  if (kF16) {  // V in fp16: exact for the bf16 values within the fp16 range
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      u32x4 w = __builtin_bit_cast(u32x4, vt[dt]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = __builtin_bit_cast(unsigned, __builtin_convertvector(
+                   (f32x2){__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xffff0000u)}, f16x2));
+      vt[dt] = __builtin_bit_cast(s16x8, w);
+    }
+  }
+
+  if (kNext) scores(sn, kn, qb);
 
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
@@ -244,7 +271,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, const unsigned char* st
 
 template <bool kF16>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [3 stages][K, V][32 keys][128 B]
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // [4 stages][K, V][32 keys][128 B]
   // Workgroup i takes KV head i % 8, so that the workgroups one XCD runs (every
   // eighth) share one head's K and V in that XCD's L2; the latest row blocks,
   // which have the most keys, start first.
@@ -340,43 +367,61 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     ws.lsum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Three LDS stages, two tiles in flight: the one barrier per tile both
-  // publishes tile it and retires tile it - 1, whose stage then takes tile it + 2.
-  issue(0, k_lo);
-  if (ntiles > 1) issue(1, k_lo + kKeys);
-  int cur = 0;  // stage of tile it
+  // Four LDS stages: at tile it the wave reads V of tile it and K of tile
+  // it + 1, tile it + 2 is in flight and tile it + 3 is issued into the stage
+  // of tile it - 1.  One barrier per tile publishes tile it + 1 and retires
+  // tile it - 1.
+  auto stage = [&](int it) { return lds + (it & (kStages - 1)) * kStage; };
+  for (int i = 0; i < 3 && i < ntiles; ++i) issue(i, k_lo + i * kKeys);
   auto sync = [&](int it) {
-    if (it + 1 < ntiles)
-      wait_vmcnt<2>();  // this wave's copies of tile it have landed (tile it + 1's may not)
+    if (it + 2 < ntiles)
+      wait_vmcnt<2>();  // this wave's copies of tiles <= it + 1 have landed (tile it + 2's may not)
     else
       wait_vmcnt<0>();
-    lds_barrier();  // every wave's copies of tile it have landed; tile it - 1 is done
-    const int prev = cur == 0 ? 2 : cur - 1;  // stage of tile it - 1 = stage of tile it + 2
-    if (it + 2 < ntiles) issue(prev, k_lo + (it + 2) * kKeys);
+    lds_barrier();  // every wave's copies of tiles <= it + 1 have landed; tile it - 1 is done
+    if (it + 3 < ntiles) issue((it + 3) & (kStages - 1), k_lo + (it + 3) * kKeys);
   };
-  auto advance = [&]() { cur = cur == 2 ? 0 : cur + 1; };
+  auto ctx = [&](int it) {
+    const int j0 = k_lo + it * kKeys;
+    // masking unless every key of the tile is visible to every row of the wave
+    return TileCtx{j0, !(j0 >= s_max && j0 + kKeys - 1 <= w_first)};
+  };
+  const RowCtx rc{c, r, s_r, s_min, w_last};
   // The tiles some row of the wave attends: keys from s_min to w_last.  Every
-  // wave takes part in every tile's barrier; the loops are split so that the
-  // accumulators only live through the middle one.
+  // wave takes part in every tile's barrier (sync(it) once for each it, in
+  // order); the accumulators live only through the middle part.
   const int t_lo = w_rows ? max(0, (s_min - k_lo) / kKeys) : ntiles;
   const int t_hi = w_rows ? min(ntiles - 1, (w_last - k_lo) / kKeys) : ntiles - 1;
   int it = 0;
-  for (; it < t_lo; ++it) {
+  for (; it < t_lo; ++it) sync(it);
+  if (t_lo <= t_hi) {
+    float sa[4][8], sb[4][8];
     sync(it);
-    advance();
+    {
+      u32x4 k0[2][2];
+      load_k(k0, stage(it), kofs);
+      scores(sa, k0, qb);
+    }
+    // two tiles per trip, so the score arrays swap roles without copies
+    for (; it + 1 < t_hi; it += 2) {
+      tile_step<kF16, true>(ws, sa, sb, stage(it), stage(it + 1), kofs, vofs, qb, c2, ctx(it), rc);
+      sync(it + 1);
+      tile_step<kF16, true>(ws, sb, sa, stage(it + 1), stage(it + 2), kofs, vofs, qb, c2, ctx(it + 1), rc);
+      sync(it + 2);
+    }
+    if (it < t_hi) {
+      tile_step<kF16, true>(ws, sa, sb, stage(it), stage(it + 1), kofs, vofs, qb, c2, ctx(it), rc);
+      sync(it + 1);
+      ++it;
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) sa[h][i] = sb[h][i];
+    }
+    tile_step<kF16, false>(ws, sa, sb, stage(it), nullptr, kofs, vofs, qb, c2, ctx(it), rc);
+    ++it;
   }
-  for (; it <= t_hi; ++it) {
-    sync(it);
-    const int j0 = k_lo + it * kKeys;
-    // masking unless every key of the tile is visible to every row of the wave
-    const bool masked = !(j0 >= s_max && j0 + kKeys - 1 <= w_first);
-    tile_step<kF16>(ws, lds + cur * kStage, kofs, vofs, qb, c2, masked, j0, c, r, s_r, s_min, w_last);
-    advance();
-  }
-  for (; it < ntiles; ++it) {
-    sync(it);
-    advance();
-  }
+  for (; it < ntiles; ++it) sync(it);
 
   if (!row_ok) return;
 #pragma unroll
