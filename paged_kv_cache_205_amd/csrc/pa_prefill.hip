@@ -436,8 +436,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const float inv = 1.f / lt;
     float* orow = a.out + ((size_t)r * kQHeads + g * kGroup + h) * kHeadDim;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)  // streaming stores: keep L2 for the keys and values
-      __builtin_nontemporal_store(ws.acc[h][dt] * inv, reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c));
+    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * c) = ws.acc[h][dt] * inv;
   }
 }
 
