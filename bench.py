@@ -341,7 +341,8 @@ def bench_prefill(args, lay):
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": (measured_traffic(PREFILL_PROFILE[args.prefill_weights], ("pa_prefill.hip", "pa_kernels.h"))
+            "traffic": (measured_traffic(PREFILL_PROFILE[args.prefill_weights],
+                                         ("pa_prefill.hip", "pa_prefill.h", "pa_kernels.h"))
                         if lay.name == "full" else None),
             "flops_per_launch": flops_launch,
             "min_hbm_bytes_per_launch": bytes_launch,

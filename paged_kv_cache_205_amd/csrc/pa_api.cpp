@@ -5,6 +5,7 @@
 #include <math.h>
 
 #include "pa_kernels.h"
+#include "pa_prefill.h"
 
 namespace {
 

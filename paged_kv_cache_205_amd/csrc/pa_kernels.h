@@ -74,22 +74,6 @@ struct FillArgs {
 
 hipError_t launch_fill(const FillArgs& a, hipStream_t stream);
 
-struct PrefillArgs {
-  const uint16_t* q;           // [T][Hq][D]
-  const uint16_t* k;           // [T][Hkv][D]
-  const uint16_t* v;
-  const int32_t* cu_tokens;    // [B+1] prompt b is rows cu_tokens[b] .. cu_tokens[b+1]-1
-  int B;
-  int T;
-  float scale_log2;            // scale * log2(e)
-  int fp16_weights;            // 0: weights as a bf16 pair with bf16 V; 1: fp16 weights and fp16 V
-  float* out;                  // [T][Hq][D]
-};
-
-// Rows T may reach (a workgroup covers 64 rows; row indices stay below 2^31).
-constexpr int kMaxPrefillRows = (1 << 30);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);

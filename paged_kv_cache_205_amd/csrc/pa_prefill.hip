@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include "pa_kernels.h"
+#include "pa_prefill.h"
 
 namespace pa {
 namespace {
