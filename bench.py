@@ -561,6 +561,16 @@ def main():
         dec_ms += [a.elapsed_time(b) for a, b in ev]
     dec_ms_mean = float(np.mean(dec_ms))
 
+    # the step's spread: each of K steps bracketed by its own events
+    step_ms = []
+    for _ in range(args.steps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        step()
+        a1.record()
+        torch.cuda.synchronize()
+        step_ms.append(a0.elapsed_time(a1))
+
     graph_ms = None
     if not args.no_graph:
         try:
@@ -622,6 +632,9 @@ def main():
         "us_per_step": round(best_ms * 1e3, 2),
         "us_per_step_stream": round(ms_step * 1e3, 2),
         "us_per_step_graph": None if graph_ms is None else round(graph_ms * 1e3, 2),
+        "us_per_step_each": {"median": round(float(np.median(step_ms)) * 1e3, 2),
+                             "min": round(float(np.min(step_ms)) * 1e3, 2),
+                             "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2)},
         "us_per_step_separate_append_decode": round(ms_step_sep * 1e3, 2),
         "seq_steps_per_s": round(lay.B / (best_ms * 1e-3), 1),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
