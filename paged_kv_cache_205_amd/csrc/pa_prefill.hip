@@ -127,6 +127,19 @@ struct RowCtx {
   int c, r, s_r, s_min, w_last;
 };
 
+// The V plane of a tile, converted in place from bf16 to fp16 by the whole
+// workgroup (thread i: bytes 16i .. 16i + 15).  Exact for the bf16 values within
+// the fp16 range.
+__device__ __forceinline__ void v_to_fp16(unsigned char* st) {
+  u32x4* p = reinterpret_cast<u32x4*>(st + kTileBytes) + threadIdx.x;
+  u32x4 w = *p;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = __builtin_bit_cast(unsigned, __builtin_convertvector(
+               (f32x2){__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xffff0000u)}, f16x2));
+  *p = w;
+}
+
 // Softmax and O^T += V^T P^T for tile `st` with scores sv, and, when kNext,
 // the scores of the next tile (K from st_next) into sn, whose MFMAs the
 // compiler can interleave with this tile's exponentials.  Masked scores become
@@ -214,18 +227,6 @@ __device__ __forceinline__ void tile_step(WaveState& ws, float (&sv)[4][8], floa
       for (int dt = 0; dt < 4; ++dt) vt[dt][i] = none ? (short)0 : vt[dt][i];
     }
   }
-  if (kF16) {  // V in fp16: exact for the bf16 values within the fp16 range
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      u32x4 w = __builtin_bit_cast(u32x4, vt[dt]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = __builtin_bit_cast(unsigned, __builtin_convertvector(
-                   (f32x2){__builtin_bit_cast(float, w[j] << 16), __builtin_bit_cast(float, w[j] & 0xffff0000u)}, f16x2));
-      vt[dt] = __builtin_bit_cast(s16x8, w);
-    }
-  }
-
   if (kNext) scores(sn, kn, qb);
 
 #pragma unroll
@@ -373,7 +374,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // of tile it - 1.  One barrier per tile publishes tile it + 1 and retires
   // tile it - 1.
   auto stage = [&](int it) { return lds + (it & (kStages - 1)) * kStage; };
+  // In fp16 mode the workgroup converts tile it + 1's V in place at tile it
+  // (tile 0's before the first tile), so each V element is converted once.
   for (int i = 0; i < 3 && i < ntiles; ++i) issue(i, k_lo + i * kKeys);
+  if (kF16) {
+    if (ntiles >= 3)
+      wait_vmcnt<4>();  // this wave's copies of tile 0 have landed
+    else if (ntiles == 2)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    v_to_fp16(stage(0));
+  }
   auto sync = [&](int it) {
     if (it + 2 < ntiles)
       wait_vmcnt<2>();  // this wave's copies of tiles <= it + 1 have landed (tile it + 2's may not)
@@ -381,6 +394,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       wait_vmcnt<0>();
     lds_barrier();  // every wave's copies of tiles <= it + 1 have landed; tile it - 1 is done
     if (it + 3 < ntiles) issue((it + 3) & (kStages - 1), k_lo + (it + 3) * kKeys);
+    if (kF16 && it + 1 < ntiles) v_to_fp16(stage(it + 1));  // read at tile it + 1, after the next barrier
   };
   auto ctx = [&](int it) {
     const int j0 = k_lo + it * kKeys;
