@@ -1,0 +1,101 @@
+"""The library's launches captured in a HIP graph (through torch.cuda.CUDAGraph)
+replay to the eager results: each graph is replayed several times with eager
+work of the program's own and synchronisations in between, and every replay is
+compared with the eager call bit for bit (both paths are deterministic: the
+decode merges its splits in split order and resets its own counters, so no
+memset sits in the graph).  Also checked against the FP64 oracle once."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode_ref, prefill_ref
+from paged_kv_cache_205_amd import ops, synth
+from tests.helpers import check_close, say
+from tests.test_oracle import rand_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.load()
+
+
+def capture(fn):
+    """Capture fn() on a side stream after one eager warm-up call; returns the graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_fused_append_decode_replays():
+    lay = synth.small()
+    l = 5
+    k_pool, v_pool = synth.make_pools(lay, "cuda", layers=[l])
+    x = synth.step_inputs(lay, l, "cuda")
+    bt = torch.from_numpy(lay.block_tables[l]).cuda()
+    sl = torch.from_numpy(lay.seq_lens).cuda()
+    ws = ops.workspace_for(lay.B, lay.max_blocks)
+    out = torch.empty((lay.B, 32, 64), device="cuda")
+
+    def step():
+        ops.pa_append_decode(x["k_new"], x["v_new"], k_pool, v_pool, x["q"], bt, sl, lay.scale, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    pool_k, pool_v = synth.bits(k_pool), synth.bits(v_pool)
+    ref = decode_ref(synth.bits(x["q"]), pool_k, pool_v, lay.block_tables[l], lay.seq_lens, lay.scale)
+    check_close(eager.cpu().numpy(), ref, "eager fused step")
+    g = capture(step)
+    other = torch.empty_like(out)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"fused decode graph replay {rep}")
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        # the appends replayed onto the same slots: the pool is unchanged
+        assert np.array_equal(synth.bits(k_pool), pool_k) and np.array_equal(synth.bits(v_pool), pool_v)
+        # eager work of the program's own between replays (same workspace, other output)
+        ops.pa_decode(x["q"], k_pool, v_pool, bt, sl, lay.scale, out=other, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
+
+
+@pytest.mark.parametrize("weights", ["bf16x2", "fp16"])
+def test_prefill_replays(weights):
+    rng = np.random.default_rng(40)
+    lens = [1, 70, 0, 130, 33]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    qh, kh, vh = rand_bits(rng, (T, 32, 64)), rand_bits(rng, (T, 8, 64)), rand_bits(rng, (T, 8, 64))
+    dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v, cud = dev(qh), dev(kh), dev(vh), torch.from_numpy(cu).cuda()
+    out = torch.empty((T, 32, 64), device="cuda")
+
+    def step():
+        ops.pa_prefill(q, k, v, cud, 0.125, out=out, weights=weights)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    check_close(eager.cpu().numpy(), prefill_ref(qh, kh, vh, cu, 0.125), f"eager prefill {weights}")
+    g = capture(step)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"prefill ({weights}) graph replay {rep}")
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        ops.pa_prefill(q, k, v, cud, 0.125, weights=weights)  # eager work in between, fresh output
+        torch.cuda.synchronize()
