@@ -1,7 +1,9 @@
 """End to end on the GPU: the page-budget scheduler drives prefill and decode.
 
 Requests are submitted, admitted in FIFO order under page budgets, prefilled one
-at a time with pa_fill through the block tables the scheduler hands out, and
+at a time (causal attention over the prompt with pa_prefill, checked against
+prefill_ref, and its K and V rows written with pa_fill) through the block
+tables the scheduler hands out, and
 then decoded together with pa_append_decode, one token per active request per
 step, with batches that change as requests finish (some early) and others are
 admitted into the freed pages.  A host copy of the pool is kept with the
@@ -12,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import append_ref, decode_ref, fill_ref
+from oracle import append_ref, decode_ref, fill_ref, prefill_ref
 from paged_kv_cache_205_amd import ops
 from tests.helpers import check_close, say
 from tests.test_oracle import rand_bits
@@ -62,6 +64,9 @@ def test_scheduler_drives_prefill_and_decode(static):
             for l in range(LAYERS):
                 bt = sched.block_table(rid, l, MAX_BLOCKS)[None]
                 ks, vs = rand_bits(rng, (n, 8, 64)), rand_bits(rng, (n, 8, 64))
+                qs = rand_bits(rng, (n, 32, 64))
+                att = ops.pa_prefill(dev(qs), dev(ks), dev(vs), dev(cu), 0.125).cpu().numpy()
+                check_close(att, prefill_ref(qs, ks, vs, cu, 0.125), f"prefill of request {rid} layer {l}")
                 ops.pa_fill(dev(ks), dev(vs), k_pool, v_pool, dev(bt), dev(cu))
                 k_host, v_host = fill_ref(k_host, v_host, ks, vs, bt, None, cu)
         # a request whose processed prefix reached its budget has produced its last token;
