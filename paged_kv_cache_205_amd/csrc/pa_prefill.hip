@@ -13,15 +13,20 @@
 //   S^T = K Q^T        v_mfma_f32_16x16x32_bf16, A = K (16 keys x 32 dims from
 //                      LDS), B = Q^T (registers); lane (t, c) gets keys
 //                      4c..4c+3 (and 16 + 4c..) of query t;
-//   O^T += V^T P^T     v_mfma_f32_16x16x32_bf16, B = P^T: the lane's 8 weights,
-//                      in the order its scores arrived (keys 4c.., 16+4c..), so P
-//                      needs no shuffle; A = V^T read in the same key order; the
-//                      weights go in as a bf16 high part plus a bf16 remainder,
-//                      two MFMAs, for at most 2^-16 relative error per weight.
+//   O^T += V^T P^T     16x16x32 MFMA, B = P^T: the lane's 8 weights, in the
+//                      order its scores arrived (keys 4c.., 16+4c..), so P needs
+//                      no shuffle; A = V^T from transposing LDS reads in the
+//                      same key order.  Two weight modes:
+//                      bf16 pairs: each weight as a bf16 high part plus a bf16
+//                      remainder (two bf16 MFMAs, at most 2^-16 relative error
+//                      per weight), V in bf16, row sums added per lane;
+//                      fp16: each weight rounded to fp16 (one f16 MFMA), V
+//                      converted to fp16 in LDS once per tile by the
+//                      workgroup, and the row sum taken over the same rounded
+//                      weights by one more MFMA against a tile of ones.
 // The softmax is the FP32 online one: a running maximum per (query, head),
 // common to the 4 lanes that hold the query, raised (with a rescale) only when
-// a tile exceeds it by more than 2^8 (the weights stay below 2^8); the row sums
-// are kept per lane and added at the end.
+// a tile exceeds it by more than 2^8 (the weights stay below 2^8).
 // Keys before the query's prompt or after the query are masked (the tile is
 // checked once per wave; only boundary tiles pay for the per-element mask).
 // K and V tiles are copied into LDS by the DMA path (a ring of four stages,
