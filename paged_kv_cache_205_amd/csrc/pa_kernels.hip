@@ -489,6 +489,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 constexpr int kTargetItems = 192;
 constexpr int kAutoMinPages = 8;
 constexpr int kMaxSplitPages = 128;
+// Length buckets for handing out single-split items longest first: bucket k
+// holds page counts down from kMaxSplitPages - 16k (the last one down to 0).
+constexpr int kLenBuckets = 8;
+__device__ __forceinline__ int len_bucket_of(int np) { return min(kLenBuckets - 1, (kMaxSplitPages - np) / 16); }
 
 __host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages) {
   return min(kMaxSplitPages, max(kAutoMinPages, (total_pages + kTargetItems - 1) / kTargetItems));
@@ -544,6 +548,8 @@ struct PlanLds {
   int first[2];        // (sequence, split) of item blockIdx.x
   int pp;              // pages per split
   int uniform_ns;      // as in ItemPlan
+  int by_length;       // single-split items are ordered longest first (sC holds the order)
+  int len_bucket[kLenBuckets][8];  // single-split sequences per length bucket and wave
 };
 struct ItemPlan {
   int pp, n_multi, n_items;
@@ -614,6 +620,7 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     if (threadIdx.x == 0) {  // read back only after later barriers
       pl->pp = pp;
       pl->uniform_ns = ns;
+      pl->by_length = 0;
       sA[B] = p.n_multi;
       sC[B] = p.n_items - p.n_multi;
     }
@@ -641,6 +648,10 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     n_single += xc;
   }
   const int i0 = blockIdx.x;
+  // When the queue hands out items and they are long on average, the
+  // single-split items go longest first (by 16-page length bucket, into sC), so
+  // that no long item starts late; otherwise they keep sequence order.
+  const bool by_length = n_multi + n_single > (int)gridDim.x && total_pages >= 16 * (n_multi + n_single);
   for (int b = b0; b < b1; ++b) {
     const int ns = nsplit_of(sL[b], pp);
     sA[b] = oa;
@@ -649,7 +660,7 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
       pl->first[0] = b;
       pl->first[1] = i0 - oa;
     }
-    if (ns == 1 && i0 == n_multi + oc) {
+    if (!by_length && ns == 1 && i0 == n_multi + oc) {
       pl->first[0] = b;
       pl->first[1] = 0;
     }
@@ -661,6 +672,57 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     sC[B] = n_single;
     pl->pp = pp;
     pl->uniform_ns = 0;
+    pl->by_length = by_length;
+  }
+  if (by_length) {
+    // Every workgroup must derive the same order, so it is a stable one: by
+    // length bucket, and by sequence within a bucket (block-wide scans of the
+    // per-thread bucket counts; no atomics).  Single-split sequences have at
+    // most pp <= kMaxSplitPages pages.
+    auto pages_of = [](int L) { return L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0; };
+    int cnt[kLenBuckets], incl[kLenBuckets];
+#pragma unroll
+    for (int k = 0; k < kLenBuckets; ++k) cnt[k] = 0;
+    for (int b = b0; b < b1; ++b)
+      if (nsplit_of(sL[b], pp) == 1) {
+        const int kb = len_bucket_of(pages_of(sL[b]));
+#pragma unroll
+        for (int k = 0; k < kLenBuckets; ++k) cnt[k] += k == kb;
+      }
+#pragma unroll
+    for (int k = 0; k < kLenBuckets; ++k) {
+      incl[k] = wave_inclusive_scan(cnt[k]);
+      if (lane == 63) pl->len_bucket[k][w] = incl[k];
+    }
+    lds_barrier();
+    int next[kLenBuckets];  // this thread's next slot in each bucket
+    int start = 0;
+#pragma unroll
+    for (int k = 0; k < kLenBuckets; ++k) {
+      int before = 0, total = 0;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int x = pl->len_bucket[k][v];
+        before += v < w ? x : 0;
+        total += x;
+      }
+      next[k] = start + before + incl[k] - cnt[k];
+      start += total;
+    }
+    for (int b = b0; b < b1; ++b)  // sC[0 .. n_single-1]: the order (sC[B] keeps the count)
+      if (nsplit_of(sL[b], pp) == 1) {
+        const int kb = len_bucket_of(pages_of(sL[b]));
+        int slot = 0;
+#pragma unroll
+        for (int k = 0; k < kLenBuckets; ++k)
+          if (k == kb) slot = next[k]++;
+        sC[slot] = b;
+      }
+    lds_barrier();
+    if (threadIdx.x == 0 && i0 >= n_multi && i0 < n_multi + n_single) {
+      pl->first[0] = sC[i0 - n_multi];
+      pl->first[1] = 0;
+    }
   }
   lds_barrier();
   p.uniform_ns = 0;
@@ -805,7 +867,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
         b = __builtin_amdgcn_readfirstlane(owner_of(sA, B, i));
         s = i - __builtin_amdgcn_readfirstlane(sA[b]);
       } else {
-        b = __builtin_amdgcn_readfirstlane(owner_of(sC, B, i - n_multi));
+        b = __builtin_amdgcn_readfirstlane(plan_lds.by_length ? sC[i - n_multi] : owner_of(sC, B, i - n_multi));
         s = 0;
       }
       L = __builtin_amdgcn_readfirstlane(sL[b]);
