@@ -481,10 +481,12 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 //           clamped to [8, 128] (so a batch yields about 192 large items);
 //   nsplit  ceil(npages / pp) splits per sequence (1 for an empty sequence);
 //   items   first every split of the multi-split sequences (sequence-major),
-//           then the single-split sequences.  Workgroup w starts with item w;
-//           if there are more items than workgroups the rest are handed out
-//           by an atomic queue.  Long sequences' splits, the largest items,
-//           start first, and no workgroup is launched without work.
+//           then the single-split sequences (longest first, by 16-page
+//           bucket, when the queue is in use and items are long on average).
+//           Workgroup w starts with item w; if there are more items than
+//           workgroups the rest are handed out by an atomic queue.  Long
+//           sequences' splits, the largest items, start first, and no
+//           workgroup is launched without work.
 
 constexpr int kTargetItems = 192;
 constexpr int kAutoMinPages = 8;
