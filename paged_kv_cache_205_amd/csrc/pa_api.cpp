@@ -56,11 +56,12 @@ int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) 
   return PA_OK;
 }
 
-// Workgroups the decode grid gets: an upper bound of the number of work items,
-// capped at what the GPU holds at once (2 workgroups per CU while the plan's
-// LDS fits beside the page ring, else 1).  *bounded is set when the bound fits,
-// i.e. every item has a workgroup of its own.
-int decode_grid(int32_t B, int32_t max_blocks, const Plan& p, bool* bounded) {
+// Workgroups the decode grid gets: an upper bound of the number of work items
+// of a batch with one page count, capped at what the GPU holds at once (2
+// workgroups per CU while the plan's LDS fits beside the page ring, else 1).
+// Items beyond the grid (a larger batch, or mixed lengths, which plan smaller
+// items) are handed out by the queue.
+int decode_grid(int32_t B, int32_t max_blocks, const Plan& p) {
   uint64_t items;
   if (p.part_pages > 0) {
     items = (uint64_t)B * p.S;
@@ -78,7 +79,6 @@ int decode_grid(int32_t B, int32_t max_blocks, const Plan& p, bool* bounded) {
     cus = n;
   const int per_cu = pa::decode_lds_bytes(B) <= 80 * 1024 ? 2 : 1;
   const uint64_t cap = (uint64_t)cus * per_cu;
-  *bounded = items <= cap;
   return (int)(items < cap ? items : cap);
 }
 
@@ -235,9 +235,9 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.guess_pp = plan.part_pages > 0 ? plan.part_pages : pa::auto_split_pages((long long)B * max_blocks);
   a.guess_ns = (max_blocks + a.guess_pp - 1) / a.guess_pp;
   a.guess_magic = a.guess_ns > 1 ? (uint32_t)(((1ull << 32) + a.guess_ns - 1) / a.guess_ns) : 0u;
-  bool bounded = false;
-  const int grid = decode_grid(B, max_blocks, plan, &bounded);
-  a.queue = bounded ? nullptr : reinterpret_cast<int*>(ws + plan.off_q);
+  const int grid = decode_grid(B, max_blocks, plan);
+  // the kernel uses the queue only when the plan has more items than the grid
+  a.queue = reinterpret_cast<int*>(ws + plan.off_q);
   if (pa::launch_decode(a, grid, fused_append, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }

@@ -488,7 +488,8 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 //           sequences' splits, the largest items, start first, and no
 //           workgroup is launched without work.
 
-constexpr int kTargetItems = 192;
+constexpr int kTargetItems = 192;          // batches with one page count (and the host's guess)
+constexpr int kTargetItemsMixed = 512;     // batches of mixed lengths (the queue takes what exceeds the grid)
 constexpr int kAutoMinPages = 8;
 constexpr int kMaxSplitPages = 128;
 // Length buckets for handing out single-split items longest first: bucket k
@@ -496,8 +497,8 @@ constexpr int kMaxSplitPages = 128;
 constexpr int kLenBuckets = 8;
 __device__ __forceinline__ int len_bucket_of(int np) { return min(kLenBuckets - 1, (kMaxSplitPages - np) / 16); }
 
-__host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages) {
-  return min(kMaxSplitPages, max(kAutoMinPages, (total_pages + kTargetItems - 1) / kTargetItems));
+__host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages, int target = kTargetItems) {
+  return min(kMaxSplitPages, max(kAutoMinPages, (total_pages + target - 1) / target));
 }
 
 __device__ __forceinline__ int nsplit_of(int L, int pp) {
@@ -610,10 +611,14 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     all_max = max(all_max, pl->wave_max[v]);
     all_min_c = max(all_min_c, pl->wave_min[v]);
   }
-  const int pp = part_pages > 0 ? part_pages : auto_pages_per_split(total_pages);
+  // One page count for every sequence: about 192 items, which suits streaming
+  // whole pages with one item per workgroup.  Mixed lengths: about 512 smaller
+  // items, so that long sequences are not left to a few workgroups at the end.
+  const bool uniform = kPageCap - all_min_c == all_max;
+  const int pp = part_pages > 0 ? part_pages : auto_pages_per_split(total_pages, uniform ? kTargetItems : kTargetItemsMixed);
   ItemPlan p;
   p.pp = pp;
-  if (kPageCap - all_min_c == all_max) {  // uniform page count
+  if (uniform) {
     const int ns = all_max > 0 ? (all_max + pp - 1) / pp : 1;
     p.uniform_ns = ns;
     p.uniform_pages = all_max;
@@ -847,7 +852,9 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     pre.b = -1;
     primed = false;
     b = -1;
-    if (!a.queue) break;
+    // no queue when every item had a workgroup of its own (item counts re-read from LDS)
+    if (!a.queue || __builtin_amdgcn_readfirstlane(sA[B]) + __builtin_amdgcn_readfirstlane(sC[B]) <= (int)gridDim.x)
+      break;
     // Wave 0 claims the next item as soon as it is done; the first barrier also
     // ensures every wave has read the previous next_item.
     int fetched = 0;
@@ -879,7 +886,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     }
   }
   // The last workgroup to leave resets the queue for the next call.
-  if (a.queue && threadIdx.x == 0) {
+  if (a.queue && sA[B] + sC[B] > (int)gridDim.x && threadIdx.x == 0) {
     const int left = __hip_atomic_fetch_add(a.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (left == (int)gridDim.x - 1) {
       __hip_atomic_store(a.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
