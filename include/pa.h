@@ -201,11 +201,12 @@ int32_t pa_default_partition_tokens(void);
  *                s, s + S_b, s + 2 S_b, ...  With partition_tokens > 0 the splits
  *                of a sequence depend only on its own length, so its output is
  *                bit-identical whatever else is in the batch.  With 0
- *                (automatic) pp = clamp(ceil(total pages of the batch / 192), 8,
- *                128): large batches get few, long splits and small or skewed
- *                batches get more; results then may differ in rounding between
- *                batches.  When S_b > 1 the splits' partial states are merged
- *                inside the same launch.
+ *                (automatic) pp = clamp(ceil(total pages of the batch / n), 8,
+ *                128) with n = 192 when every sequence has the same page count
+ *                and 512 otherwise: large batches get few, long splits and
+ *                small or skewed batches get more; results then may differ in
+ *                rounding between batches.  When S_b > 1 the splits' partial
+ *                states are merged inside the same launch.
  *   B            at most PA_MAX_DECODE_BATCH (the work plan lives in LDS).
  *   workspace    device buffer of at least
  *                pa_decode_workspace_bytes(B, Hq, D, max_blocks, partition_tokens)

@@ -477,8 +477,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 
 // ---------------------------------------------------------------------------
 // Work plan.  Every workgroup builds the same plan in LDS from seq_lens:
-//   pp      pages per split: a.part_pages if set, else ceil(total pages / 192)
-//           clamped to [8, 128] (so a batch yields about 192 large items);
+//   pp      pages per split: a.part_pages if set, else ceil(total pages / n)
+//           clamped to [8, 128], n = 192 when every sequence has the same page
+//           count and 512 for mixed lengths (about n items);
 //   nsplit  ceil(npages / pp) splits per sequence (1 for an empty sequence);
 //   items   first every split of the multi-split sequences (sequence-major),
 //           then the single-split sequences (longest first, by 16-page
