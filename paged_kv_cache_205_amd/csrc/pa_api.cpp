@@ -10,7 +10,6 @@
 namespace {
 
 constexpr int32_t kMaxPartitionTokens = 2048;  // a split holds at most 128 pages
-constexpr int32_t kAutoMinPages = 8;           // smallest split the automatic choice makes
 constexpr int32_t kTargetItems = 192;          // automatic choice: about this many large items per call
 constexpr size_t kAlign = 256;
 
@@ -31,13 +30,14 @@ struct Plan {
 
 // With partition_tokens > 0 a sequence of L tokens has ceil(L / partition_tokens)
 // splits, independent of the rest of the batch.  With 0 the kernel picks the
-// split size from the batch's total pages (at least 8 pages per split).
+// split size from the batch's total pages (at least 4 pages per split for
+// batches of up to 64 sequences, 8 above).
 int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) {
   if (partition_tokens < 0 || partition_tokens % pa::kPageTokens != 0) return PA_ERR_SHAPE;
   int32_t min_pages;
   if (partition_tokens == 0) {
     p->part_pages = 0;
-    min_pages = kAutoMinPages;
+    min_pages = pa::auto_split_min_pages(B);
   } else {
     const int32_t pt = partition_tokens > kMaxPartitionTokens ? kMaxPartitionTokens : partition_tokens;
     p->part_pages = pt / pa::kPageTokens;
@@ -232,7 +232,7 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.S = plan.S;
   a.scale_log2 = scale * 1.4426950408889634f;
   // the plan when every sequence fills its table row
-  a.guess_pp = plan.part_pages > 0 ? plan.part_pages : pa::auto_split_pages((long long)B * max_blocks);
+  a.guess_pp = plan.part_pages > 0 ? plan.part_pages : pa::auto_split_pages((long long)B * max_blocks, B);
   a.guess_ns = (max_blocks + a.guess_pp - 1) / a.guess_pp;
   a.guess_magic = a.guess_ns > 1 ? (uint32_t)(((1ull << 32) + a.guess_ns - 1) / a.guess_ns) : 0u;
   const int grid = decode_grid(B, max_blocks, plan);

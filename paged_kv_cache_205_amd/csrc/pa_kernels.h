@@ -78,8 +78,10 @@ hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t*
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);
 size_t decode_lds_bytes(int B);
-// Pages per split that the automatic plan picks for a batch with this many pages.
-int auto_split_pages(long long total_pages);
+// Pages per split that the automatic plan picks for a batch with this many pages
+// (all with the same page count), and its smallest split for a batch of B sequences.
+int auto_split_pages(long long total_pages, int B);
+int auto_split_min_pages(int B);
 hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 

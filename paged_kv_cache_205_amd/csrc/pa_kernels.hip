@@ -478,8 +478,9 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 // ---------------------------------------------------------------------------
 // Work plan.  Every workgroup builds the same plan in LDS from seq_lens:
 //   pp      pages per split: a.part_pages if set, else ceil(total pages / n)
-//           clamped to [8, 128], n = 192 when every sequence has the same page
-//           count and 512 for mixed lengths (about n items);
+//           clamped to [m, 128], n = 192 when every sequence has the same page
+//           count and 512 for mixed lengths (about n items), m = 4 for batches
+//           of at most 64 sequences and 8 above;
 //   nsplit  ceil(npages / pp) splits per sequence (1 for an empty sequence);
 //   items   first every split of the multi-split sequences (sequence-major),
 //           then the single-split sequences (longest first, by 16-page
@@ -498,8 +499,12 @@ constexpr int kMaxSplitPages = 128;
 constexpr int kLenBuckets = 8;
 __device__ __forceinline__ int len_bucket_of(int np) { return min(kLenBuckets - 1, (kMaxSplitPages - np) / 16); }
 
-__host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages, int target = kTargetItems) {
-  return min(kMaxSplitPages, max(kAutoMinPages, (total_pages + target - 1) / target));
+// Smallest automatic split: 4 pages for batches of at most 64 sequences (their
+// items are few, so shorter ones cut the latency of each), 8 above.
+__host__ __device__ __forceinline__ int auto_min_pages(int B) { return B <= 64 ? 4 : kAutoMinPages; }
+__host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages, int target = kTargetItems,
+                                                             int minp = kAutoMinPages) {
+  return min(kMaxSplitPages, max(minp, (total_pages + target - 1) / target));
 }
 
 __device__ __forceinline__ int nsplit_of(int L, int pp) {
@@ -616,7 +621,9 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
   // whole pages with one item per workgroup.  Mixed lengths: about 512 smaller
   // items, so that long sequences are not left to a few workgroups at the end.
   const bool uniform = kPageCap - all_min_c == all_max;
-  const int pp = part_pages > 0 ? part_pages : auto_pages_per_split(total_pages, uniform ? kTargetItems : kTargetItemsMixed);
+  const int pp = part_pages > 0 ? part_pages
+                                : auto_pages_per_split(total_pages, uniform ? kTargetItems : kTargetItemsMixed,
+                                                       auto_min_pages(B));
   ItemPlan p;
   p.pp = pp;
   if (uniform) {
@@ -953,9 +960,12 @@ static size_t decode_dynamic_lds_bytes(int B) {
 
 size_t decode_lds_bytes(int B) { return decode_dynamic_lds_bytes(B) + sizeof(PlanLds) + 2 * sizeof(int); }
 
-int auto_split_pages(long long total_pages) {
-  return auto_pages_per_split((int)(total_pages < (1 << 30) ? total_pages : (1 << 30)));
+int auto_split_pages(long long total_pages, int B) {
+  return auto_pages_per_split((int)(total_pages < (1 << 30) ? total_pages : (1 << 30)), kTargetItems,
+                              auto_min_pages(B));
 }
+
+int auto_split_min_pages(int B) { return auto_min_pages(B); }
 
 hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream) {
   const size_t lds = decode_dynamic_lds_bytes(a.B);

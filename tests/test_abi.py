@@ -55,8 +55,9 @@ def test_default_partition_and_workspace_sizes(lib):
     # single split: no partials, only the per-sequence counters and the queue counter
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 2048) == 256 + 256
     assert lib.pa_decode_workspace_bytes(512, 32, 64, 8, 0) == 2048 + 256  # automatic splits have >= 8 pages
-    # automatic: partial rows for up to ceil(128 / 8) = 16 splits
-    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 0) == lib.pa_decode_workspace_bytes(64, 32, 64, 128, 128)
+    # automatic: partial rows for up to ceil(128 / 4) = 32 splits for up to 64 sequences, ceil(128 / 8) = 16 above
+    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 0) == lib.pa_decode_workspace_bytes(64, 32, 64, 128, 64)
+    assert lib.pa_decode_workspace_bytes(65, 32, 64, 128, 0) == lib.pa_decode_workspace_bytes(65, 32, 64, 128, 128)
     assert lib.pa_decode_workspace_bytes(5000, 32, 64, 128, 0) == 0  # batch above the plan limit
     # 8 splits of 256 tokens: part_o + part_m + part_l + one counter per sequence + the queue,
     # each padded to 256 bytes
