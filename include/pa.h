@@ -201,9 +201,10 @@ int32_t pa_default_partition_tokens(void);
  *                s, s + S_b, s + 2 S_b, ...  With partition_tokens > 0 the splits
  *                of a sequence depend only on its own length, so its output is
  *                bit-identical whatever else is in the batch.  With 0
- *                (automatic) pp = clamp(ceil(total pages of the batch / n), 8,
+ *                (automatic) pp = clamp(ceil(total pages of the batch / n), m,
  *                128) with n = 192 when every sequence has the same page count
- *                and 512 otherwise: large batches get few, long splits and
+ *                and 512 otherwise, and m = 4 for B <= 64, 8 above (the
+ *                smallest split): large batches get few, long splits and
  *                small or skewed batches get more; results then may differ in
  *                rounding between batches.  When S_b > 1 the splits' partial
  *                states are merged inside the same launch.
