@@ -41,7 +41,7 @@ Sources (web pages describing the samir-vllm teaching engine):
 
   evaluated in FP64 by walking the block table page by page.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * ``seq_lens[b]`` is the length after the append; decode attends every
     position t < L, including the one just appended.
   * query head h uses KV head h // G with G = Hq / Hkv (contiguous groups).

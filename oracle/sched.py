@@ -29,7 +29,7 @@ samir-vllm teaching engine):
 * Statistics: pool size, peak active requests, largest decode batch, peak
   assigned pages, admission waits, free pages ([README] --stats paragraph).
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
   * FIFO is strict: when the oldest waiting request does not fit, no younger
     one is admitted ahead of it.
   * "admission waits" counts requests that could not be admitted by the first
