@@ -56,11 +56,22 @@ int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) 
   return PA_OK;
 }
 
+// Compute units of the current device (256 on MI355X).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+    return n;
+  return 256;
+}
+
 // Workgroups the decode grid gets: an upper bound of the number of work items
 // of a batch with one page count, capped at what the GPU holds at once (2
 // workgroups per CU while the plan's LDS fits beside the page ring, else 1).
-// Items beyond the grid (a larger batch, or mixed lengths, which plan smaller
-// items) are handed out by the queue.
+// Items beyond the workgroups that take them (a larger batch, or mixed
+// lengths, which plan smaller items; batches of long items use one workgroup
+// per CU) are handed out by the queue.
+
 int decode_grid(int32_t B, int32_t max_blocks, const Plan& p) {
   uint64_t items;
   if (p.part_pages > 0) {
@@ -73,10 +84,7 @@ int decode_grid(int32_t B, int32_t max_blocks, const Plan& p) {
     const uint64_t all = (uint64_t)B * p.S;
     items = bound < all ? bound : all;
   }
-  int cus = 256, dev = 0, n = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-    cus = n;
+  const int cus = device_cus();
   const int per_cu = pa::decode_lds_bytes(B) <= 80 * 1024 ? 2 : 1;
   const uint64_t cap = (uint64_t)cus * per_cu;
   return (int)(items < cap ? items : cap);
@@ -236,6 +244,8 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.guess_ns = (max_blocks + a.guess_pp - 1) / a.guess_pp;
   a.guess_magic = a.guess_ns > 1 ? (uint32_t)(((1ull << 32) + a.guess_ns - 1) / a.guess_ns) : 0u;
   const int grid = decode_grid(B, max_blocks, plan);
+  // batches of long items run one workgroup per CU (the kernel decides from the lengths)
+  a.narrow = device_cus();
   // the kernel uses the queue only when the plan has more items than the grid
   a.queue = reinterpret_cast<int*>(ws + plan.off_q);
   if (pa::launch_decode(a, grid, fused_append, stream) != hipSuccess) return PA_ERR_LAUNCH;

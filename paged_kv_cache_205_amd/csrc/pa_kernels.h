@@ -35,6 +35,7 @@ struct DecodeArgs {
   const uint16_t* k_pool;
   const uint16_t* v_pool;
   int S;             // row stride of the partials: an upper bound of any sequence's split count
+  int narrow;        // workgroups to use when the items are long (one per CU); 0: all of the grid
   float scale_log2;  // scale * log2(e)
   uint16_t* k_pool_w;  // fused append only: the pools, writable
   uint16_t* v_pool_w;

@@ -487,10 +487,15 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 //           bucket, when the queue is in use and items are long on average).
 //           Workgroup w starts with item w; if there are more items than
 //           workgroups the rest are handed out by an atomic queue.  Long
-//           sequences' splits, the largest items, start first, and no
-//           workgroup is launched without work.
+//           sequences' splits, the largest items, start first.
+//   active  the workgroups that take items: the whole grid (two per CU) when
+//           items average fewer than 8 pages, whose latency a second
+//           workgroup per CU hides; else one per CU (a.narrow), which streams
+//           pages faster and leaves the balancing to the queue.  The others
+//           leave right after the plan.
 
 constexpr int kTargetItems = 192;          // batches with one page count (and the host's guess)
+constexpr int kLongItemPages = 8;          // items averaging this many pages run one workgroup per CU
 constexpr int kTargetItemsMixed = 512;     // batches of mixed lengths (the queue takes what exceeds the grid)
 constexpr int kAutoMinPages = 8;
 constexpr int kMaxSplitPages = 128;
@@ -505,6 +510,11 @@ __host__ __device__ __forceinline__ int auto_min_pages(int B) { return B <= 64 ?
 __host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages, int target = kTargetItems,
                                                              int minp = kAutoMinPages) {
   return min(kMaxSplitPages, max(minp, (total_pages + target - 1) / target));
+}
+
+__device__ __forceinline__ int active_workgroups(int total_pages, int n_items, int narrow) {
+  const int grid = (int)gridDim.x;
+  return narrow > 0 && narrow < grid && total_pages >= kLongItemPages * n_items ? narrow : grid;
 }
 
 __device__ __forceinline__ int nsplit_of(int L, int pp) {
@@ -558,10 +568,11 @@ struct PlanLds {
   int pp;              // pages per split
   int uniform_ns;      // as in ItemPlan
   int by_length;       // single-split items are ordered longest first (sC holds the order)
+  int active;          // workgroups that take items (see the plan above)
   int len_bucket[kLenBuckets][8];  // single-split sequences per length bucket and wave
 };
 struct ItemPlan {
-  int pp, n_multi, n_items;
+  int pp, n_multi, n_items, active;
   int uniform_ns;     // > 0: every sequence has this many splits, item i is (i / ns, i % ns)
   int uniform_pages;  // with uniform_ns > 0: every sequence's page count
 };
@@ -596,8 +607,8 @@ __device__ __forceinline__ PlanLengths plan_lengths(const int32_t* __restrict__ 
   return x;
 }
 
-__device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_pages, int* sL, int* sA, int* sC,
-                                                PlanLds* pl) {
+__device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_pages, int narrow, int* sL, int* sA,
+                                                int* sC, PlanLds* pl) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int per = (B + 511) / 512;
   const int b0 = min(B, (int)threadIdx.x * per), b1 = min(B, b0 + per);
@@ -632,10 +643,14 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     p.uniform_pages = all_max;
     p.n_items = B * ns;
     p.n_multi = ns > 1 ? p.n_items : 0;
-    if (threadIdx.x == 0) {  // read back only after later barriers
+    p.active = active_workgroups(total_pages, p.n_items, narrow);
+    // No barrier follows: every wave writes these (equal) values itself, so
+    // that each wave's later reads see them.
+    if ((threadIdx.x & 63) == 0) {
       pl->pp = pp;
       pl->uniform_ns = ns;
       pl->by_length = 0;
+      pl->active = p.active;
       sA[B] = p.n_multi;
       sC[B] = p.n_items - p.n_multi;
     }
@@ -663,10 +678,11 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     n_single += xc;
   }
   const int i0 = blockIdx.x;
+  const int active = active_workgroups(total_pages, n_multi + n_single, narrow);
   // When the queue hands out items and they are long on average, the
   // single-split items go longest first (by 16-page length bucket, into sC), so
   // that no long item starts late; otherwise they keep sequence order.
-  const bool by_length = n_multi + n_single > (int)gridDim.x && total_pages >= 16 * (n_multi + n_single);
+  const bool by_length = n_multi + n_single > active && total_pages >= 16 * (n_multi + n_single);
   for (int b = b0; b < b1; ++b) {
     const int ns = nsplit_of(sL[b], pp);
     sA[b] = oa;
@@ -688,6 +704,7 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     pl->pp = pp;
     pl->uniform_ns = 0;
     pl->by_length = by_length;
+    pl->active = active;
   }
   if (by_length) {
     // Every workgroup must derive the same order, so it is a stable one: by
@@ -744,6 +761,7 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
   p.uniform_pages = 0;
   p.n_multi = n_multi;
   p.n_items = n_multi + n_single;
+  p.active = active;
   return p;
 }
 
@@ -818,14 +836,14 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   }
 
   const PlanLengths lens = plan_lengths(a.seq_lens, B, len0, sL);
-  const ItemPlan plan = plan_finish(lens, B, a.part_pages, sL, sA, sC, &plan_lds);
+  const ItemPlan plan = plan_finish(lens, B, a.part_pages, a.narrow, sL, sA, sC, &plan_lds);
   // values read back from LDS are the same in every lane: keep them scalar
   const int ppu = __builtin_amdgcn_readfirstlane(plan.pp);
   const int uns = __builtin_amdgcn_readfirstlane(plan.uniform_ns);
 
   // Item blockIdx.x first.
   int b = -1, s = 0, L = 0, nsplit = 1, n = 0;
-  if ((int)blockIdx.x < __builtin_amdgcn_readfirstlane(plan.n_items)) {
+  if ((int)blockIdx.x < min(__builtin_amdgcn_readfirstlane(plan.n_items), __builtin_amdgcn_readfirstlane(plan.active))) {
     if (uns > 0 && pre.b >= 0 && __builtin_amdgcn_readfirstlane(plan.uniform_pages) == a.max_blocks &&
         ppu == a.guess_pp) {
       // every sequence fills its table row: the item is the guessed one
@@ -851,7 +869,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   bool primed = prime_b >= 0 && b == prime_b && s == s_g && nsplit == ns_g;
   if (prime_b >= 0 && !primed) wait_vmcnt<0>();  // unused copies land before their slots are reused
 
-  // When the grid may hold fewer workgroups than items, later items come from
+  // When there are more items than active workgroups, later items come from
   // a queue counter, so that workgroups busy with long splits take no further
   // work.  Nothing of the plan is kept in registers across an item: the next
   // item is derived from the plan in LDS.
@@ -861,13 +879,13 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     primed = false;
     b = -1;
     // no queue when every item had a workgroup of its own (item counts re-read from LDS)
-    if (!a.queue || __builtin_amdgcn_readfirstlane(sA[B]) + __builtin_amdgcn_readfirstlane(sC[B]) <= (int)gridDim.x)
-      break;
+    const int act = __builtin_amdgcn_readfirstlane(plan_lds.active);
+    if (!a.queue || __builtin_amdgcn_readfirstlane(sA[B]) + __builtin_amdgcn_readfirstlane(sC[B]) <= act) break;
     // Wave 0 claims the next item as soon as it is done; the first barrier also
     // ensures every wave has read the previous next_item.
     int fetched = 0;
     if (threadIdx.x == 0)
-      fetched = (int)gridDim.x + __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      fetched = act + __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (threadIdx.x == 0) next_item = fetched;
     __syncthreads();
@@ -893,8 +911,9 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
       n = (n - s + nsplit - 1) / nsplit;
     }
   }
-  // The last workgroup to leave resets the queue for the next call.
-  if (a.queue && sA[B] + sC[B] > (int)gridDim.x && threadIdx.x == 0) {
+  // The last workgroup to leave (every workgroup of the grid counts itself)
+  // resets the queue for the next call.
+  if (a.queue && sA[B] + sC[B] > plan_lds.active && threadIdx.x == 0) {
     const int left = __hip_atomic_fetch_add(a.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (left == (int)gridDim.x - 1) {
       __hip_atomic_store(a.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
