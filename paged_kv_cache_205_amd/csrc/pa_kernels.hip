@@ -592,12 +592,17 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 struct PlanLengths {
   int pages, pmax, pmin_c;  // this thread's page sum, largest count, kPageCap - smallest count
 };
-__device__ __forceinline__ PlanLengths plan_lengths(const int32_t* __restrict__ seq_lens, int B, int len0, int* sL) {
+constexpr int kLensPerThread = 8;  // lengths a thread of the plan handles, at most (B <= 4096)
+static_assert(kMaxDecodeBatch <= 512 * kLensPerThread, "plan: lengths per thread");
+__device__ __forceinline__ PlanLengths plan_lengths(int B, const int (&lens)[kLensPerThread], int* sL) {
   const int per = (B + 511) / 512;
-  const int b0 = min(B, (int)threadIdx.x * per), b1 = min(B, b0 + per);
+  const int b0 = min(B, (int)threadIdx.x * per);
   PlanLengths x{0, 0, 0};
-  for (int b = b0; b < b1; ++b) {
-    const int L = b == b0 ? len0 : seq_lens[b];
+#pragma unroll
+  for (int k = 0; k < kLensPerThread; ++k) {
+    const int b = b0 + k;
+    if (k >= per || b >= B) break;
+    const int L = lens[k];
     sL[b] = L;
     const int np = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
     x.pages += np;
@@ -780,9 +785,13 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   int* sC = sA + B + 1;   // [B+1] single-split item prefix
 
 
-  // The first of this thread's lengths.
+  // This thread's lengths for the plan (sequences t*per .. t*per + per - 1),
+  // all loaded at once.
   const int per = (B + 511) / 512;
-  const int len0 = a.seq_lens[min((int)threadIdx.x * per, B - 1)];
+  int lens[kLensPerThread];
+#pragma unroll
+  for (int k = 0; k < kLensPerThread; ++k)
+    lens[k] = k < per ? a.seq_lens[min((int)threadIdx.x * per + k, B - 1)] : 0;
 
   // While the plan is built, load the table row, q and the appended rows of
   // this workgroup's first item as it would be if every sequence filled its
@@ -817,9 +826,10 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   // guessed item's first pages now, so that the plan overlaps them.
   // They are used if the plan confirms the guess, else drained.
   const DmaOffsets doff = dma_offsets(threadIdx.x & 63, threadIdx.x >> 6);
-  // the length and the table row are waited for here, so that no wait placed
+  // the lengths and the table row are waited for here, so that no wait placed
   // for them later includes the copies
-  asm volatile("" ::"v"(len0), "v"(pre.id0), "v"(pre.id1));
+  asm volatile("" ::"v"(lens[0]), "v"(lens[1]), "v"(lens[2]), "v"(lens[3]), "v"(lens[4]), "v"(lens[5]),
+               "v"(lens[6]), "v"(lens[7]), "v"(pre.id0), "v"(pre.id1));
   int prime_b = -1;
   if (pre.b >= 0 && (L_g + kPageTokens - 1) / kPageTokens == a.max_blocks) {
     const int g = threadIdx.x >> 6;
@@ -835,8 +845,8 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     prime_b = pre.b;
   }
 
-  const PlanLengths lens = plan_lengths(a.seq_lens, B, len0, sL);
-  const ItemPlan plan = plan_finish(lens, B, a.part_pages, a.narrow, sL, sA, sC, &plan_lds);
+  const PlanLengths pl_lens = plan_lengths(B, lens, sL);
+  const ItemPlan plan = plan_finish(pl_lens, B, a.part_pages, a.narrow, sL, sA, sC, &plan_lds);
   // values read back from LDS are the same in every lane: keep them scalar
   const int ppu = __builtin_amdgcn_readfirstlane(plan.pp);
   const int uns = __builtin_amdgcn_readfirstlane(plan.uniform_ns);
