@@ -496,7 +496,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 
 constexpr int kTargetItems = 192;          // batches with one page count (and the host's guess)
 constexpr int kLongItemPages = 8;          // items averaging this many pages run one workgroup per CU
-constexpr int kTargetItemsMixed = 512;     // batches of mixed lengths (the queue takes what exceeds the grid)
+constexpr int kTargetItemsMixed = 512;     // batches of mixed lengths (the queue takes what the active workgroups do not)
 constexpr int kAutoMinPages = 8;
 constexpr int kMaxSplitPages = 128;
 // Length buckets for handing out single-split items longest first: bucket k
