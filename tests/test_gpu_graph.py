@@ -99,3 +99,38 @@ def test_prefill_replays(weights):
         assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
         ops.pa_prefill(q, k, v, cud, 0.125, weights=weights)  # eager work in between, fresh output
         torch.cuda.synchronize()
+
+
+def test_queued_decode_replays():
+    """A mixed batch whose items exceed the workgroups that take them (300
+    sequences, one workgroup per CU, the rest from the queue): every replay
+    equals the eager call bit for bit, so the queue and the split counters are
+    back at zero after each call, also inside a graph."""
+    lay = synth.fragmented(B=300, n_layers=1)
+    k_pool, v_pool = synth.make_pools(lay, "cuda")
+    x = synth.step_inputs(lay, 0, "cuda")
+    bt = torch.from_numpy(lay.block_tables[0]).cuda()
+    sl = torch.from_numpy(lay.seq_lens).cuda()
+    ws = ops.workspace_for(lay.B, lay.max_blocks)
+    out = torch.empty((lay.B, 32, 64), device="cuda")
+
+    def step():
+        ops.pa_append_decode(x["k_new"], x["v_new"], k_pool, v_pool, x["q"], bt, sl, lay.scale, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    sample = [0, 1, 2, 3, int(np.argmax(lay.seq_lens)), lay.B - 1]
+    pool_k, pool_v = synth.bits(k_pool), synth.bits(v_pool)
+    ref = decode_ref(synth.bits(x["q"]), pool_k, pool_v, lay.block_tables[0], lay.seq_lens, lay.scale, batch=sample)
+    check_close(eager.cpu().numpy()[sample], ref[sample], "eager queued step")
+    g = capture(step)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"queued decode graph replay {rep}")
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        other = ops.pa_decode(x["q"], k_pool, v_pool, bt, sl, lay.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(other, eager)
