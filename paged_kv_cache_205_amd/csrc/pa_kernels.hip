@@ -18,6 +18,7 @@
 #include "pa_kernels.h"
 
 #include <algorithm>
+#include <atomic>
 
 namespace pa {
 
@@ -996,18 +997,29 @@ int auto_split_pages(long long total_pages, int B) {
 
 int auto_split_min_pages(int B) { return auto_min_pages(B); }
 
+// Raises a decode kernel's dynamic LDS limit to what the largest batch needs,
+// once per device (the attribute belongs to the device the call is made on).
+static hipError_t allow_decode_lds(const void* kernel, int which) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> done[2][kMaxDevices];
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev >= 0 && dev < kMaxDevices && done[which][dev].load(std::memory_order_acquire)) return hipSuccess;
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)decode_dynamic_lds_bytes(kMaxDecodeBatch));
+  if (err == hipSuccess && dev >= 0 && dev < kMaxDevices) done[which][dev].store(1, std::memory_order_release);
+  return err;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream) {
   const size_t lds = decode_dynamic_lds_bytes(a.B);
   if (fused_append) {
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_dynamic_lds_bytes(kMaxDecodeBatch));
+    const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<true>), 1);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
   } else {
-    static const hipError_t attr =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(decode_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_dynamic_lds_bytes(kMaxDecodeBatch));
+    const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<false>), 0);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
   }
