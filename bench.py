@@ -53,6 +53,9 @@ PREFILL_METRIC = ("prefill attention: TFLOP/s (causal GQA, 4*D flops per attende
                   "µs/step at batch 64×2047")
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FILL_METRIC = "prefill page fill: effective GB/s (K/V rows read + written), µs/step at batch 64×2047"
+ROPE_METRIC = ("RoPE + KV append: effective GB/s (q, new K/V and the table row read; rotated q and the pool "
+               "rows written), µs/step at batch 64×2048")
+ROPE_BYTES_PER_SEQ = 4096 + 4096 + 2 * 1024 + 2 * 1024 + 256  # q in/out, K/V in/out, one table row
 
 
 def measured_traffic(profile=None, sources=("pa_kernels.hip", "pa_kernels.h")):
@@ -194,6 +197,140 @@ def bench_fill(args, lay):
             "unit": "GB/s",
             "frac": round(bytes_launch / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(FILL_PROFILE) if lay.name == "full" else None,
+            "bytes_per_launch": bytes_launch,
+            "mean_launch_us": round(launch_ms * 1e3, 3),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def _oracle_rope(item):
+    """rope_append_ref for one (layer, sequence) of the sample, into a one-page pool."""
+    from oracle.rope import rope_append_ref
+    l, b = item
+    d = _CPU[("rope", l)]
+    one = np.zeros((1, 16, 8, 64), np.uint16)
+    rope_append_ref(d["q"][b:b + 1], d["k"][b:b + 1], d["v"][b:b + 1], d["table"], one, one.copy(),
+                    np.zeros((1, 128), np.int32), d["L"][b:b + 1], np.zeros((1, 32, 64), np.uint16))
+    return 1
+
+
+def cpu_baseline_rope(lay, n_layers: int, workers: int):
+    """Time the oracle's RoPE + append on every sequence of the first n_layers layers."""
+    import torch
+    from paged_kv_cache_205_amd import synth
+    torch.set_num_threads(1)
+    layers = list(range(min(n_layers, lay.n_layers)))
+    table = synth.rope_table(2048).numpy()
+    for l in layers:
+        x = synth.step_inputs(lay, l, "cpu")
+        _CPU[("rope", l)] = dict(q=synth.bits(x["q"]), k=synth.bits(x["k_new"]), v=synth.bits(x["v_new"]),
+                                 table=table, L=lay.seq_lens.astype(np.int32))
+    items = [(l, b) for l in layers for b in range(lay.B)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        n = sum(pool.map(_oracle_rope, items, chunksize=4))
+    tw = time.perf_counter() - t0
+    return {
+        "value": round(n * ROPE_BYTES_PER_SEQ / tw / 1e9, 6),
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"layers 0..{layers[-1]} of the same step, all {lay.B} sequences each ({n} sequence-layers): "
+                  f"rope_append_ref (NumPy FP32) in {workers} worker processes, {tw:.2f} s wall",
+        "seconds": round(tw, 3),
+    }
+
+
+def bench_rope(args, lay):
+    """One step = one pa_rope_append per layer: every sequence's query and new key rotated at
+    position L - 1, the key and value appended."""
+    cpu = None
+    if not args.no_cpu:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"cpu baseline (rope): oracle on {workers} workers ...")
+        cpu = cpu_baseline_rope(lay, lay.n_layers, workers)
+    import torch
+    from paged_kv_cache_205_amd import ops, synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.load()
+    dev = "cuda"
+    k_pool, v_pool = synth.make_pools(lay, dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
+    table = synth.rope_table(2048, device=dev)
+    inputs = [synth.step_inputs(lay, l, dev) for l in range(lay.n_layers)]
+    q_out = [torch.empty_like(x["q"]) for x in inputs]
+    live = int((lay.seq_lens > 0).sum())
+    bytes_launch = live * ROPE_BYTES_PER_SEQ
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(lay.n_layers):
+            x = inputs[l]
+            ops.pa_rope_append(x["q"], x["k_new"], x["v_new"], table, k_pool, v_pool, bt[l], seq_lens, q_out=q_out[l])
+
+    def timed(run):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            run()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    for _ in range(args.warmup):
+        step()
+    ms_stream = timed(step)
+    # A launch takes a few microseconds, less than the host's cost of issuing
+    # it, so the step is timed as a captured graph of its 16 launches (the
+    # stream timing is reported beside it).
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    ms_step = timed(graph.replay)
+    launch_ms = ms_step / lay.n_layers
+    value = bytes_launch * lay.n_layers / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": ROPE_METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"RoPE + append of {lay.name}: B={lay.B} new tokens per layer, {lay.n_layers} layers, "
+                        f"32 q / 8 kv heads, D=64, 16-token BF16 pages, FP32 table of 2048 positions",
+            "batch": lay.B,
+            "layers": lay.n_layers,
+            "bytes_per_step": bytes_launch * lay.n_layers,
+            "timing": "graph replay of the 16 launches",
+            "parallelism": "single GPU",
+        },
+        "us_per_step": round(ms_step * 1e3, 2),
+        "us_per_step_stream": round(ms_stream * 1e3, 2),
+        "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {
+            "kernel": "rope_append_kernel (one launch per layer, one wave per sequence)",
+            "bound": "hbm",
+            "achieved": round(bytes_launch / (launch_ms * 1e-3) / 1e9, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(bytes_launch / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": None,
             "bytes_per_launch": bytes_launch,
             "mean_launch_us": round(launch_ms * 1e3, 3),
         },
@@ -456,9 +593,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-layers", type=int, default=8, help="layers of the workload the oracle runs on")
     ap.add_argument("--no-graph", action="store_true", help="skip the captured-graph timing")
-    ap.add_argument("--op", choices=("decode", "fill", "prefill"), default="decode",
+    ap.add_argument("--op", choices=("decode", "fill", "prefill", "rope"), default="decode",
                     help="decode: the decode step (default); fill: the prefill page fill; "
-                         "prefill: the causal prefill attention")
+                         "prefill: the causal prefill attention; rope: RoPE at the position + append")
     ap.add_argument("--cpu-prompts", type=int, default=192, help="prompts (layer by layer) the prefill oracle runs on")
     ap.add_argument("--prefill-weights", choices=("bf16x2", "fp16"), default="bf16x2",
                     help="prefill: weights as bf16 pairs (default) or fp16 weights with fp16 V")
@@ -478,6 +615,9 @@ def main():
         return
     if args.op == "prefill":
         bench_prefill(args, lay)
+        return
+    if args.op == "rope":
+        bench_rope(args, lay)
         return
 
     cpu = None

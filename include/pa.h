@@ -108,6 +108,43 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
               int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
 
 /*
+ * pa_rope_append - rotate this step's query and new key by RoPE at the token's
+ * absolute position, then write the new K and V into the page slot.
+ * ([README] feature list: RoPE is applied to the projected queries and keys
+ * before attention; KV page pool item: decode appends one new token at its
+ * absolute RoPE position.  The pages print no RoPE constants or pairing.)
+ *
+ * For each b with L = seq_lens[b] >= 1, pos = L - 1 < max_pos, and a table
+ * entry page = block_table[b][pos/16] in [0, num_pages):
+ *   q_out[b][h]          = rot(q[b][h])       for the Hq query heads
+ *   k_pool[page][slot][g] = rot(k_new[b][g])  slot = pos % 16, g < Hkv
+ *   v_pool[page][slot][g] = v_new[b][g]       (bit copy)
+ * with, for i < 32, c_i = cos_sin[pos][i] and s_i = cos_sin[pos][32 + i]:
+ *   rot(x)[i]      = x[i] c_i - x[i + 32] s_i
+ *   rot(x)[i + 32] = x[i + 32] c_i + x[i] s_i
+ * Each product and the difference or sum is one FP32 operation rounded to
+ * nearest (no fused multiply-add); the result is rounded to BF16 to nearest,
+ * ties to even (a NaN stays a quiet NaN).  The table carries the base and any
+ * frequency scaling.  Other sequences are skipped: their q_out rows are not
+ * written and nothing is appended.
+ *
+ *   q, q_out      bf16 [B][Hq][D] (q_out written; it may not overlap q)
+ *   k_new, v_new  bf16 [B][Hkv][D]
+ *   cos_sin       fp32 [max_pos][D]
+ *   k_pool, v_pool bf16 [num_pages][16][Hkv][D] (written)
+ *   block_table   int32 [B][max_blocks] of one layer
+ *   seq_lens      int32 [B]
+ * B in 0 .. PA_MAX_DECODE_BATCH.  The caller assigns the page of block
+ * (L-1)/16 before the call, as for pa_append.  Returns PA_OK, PA_ERR_SHAPE,
+ * PA_ERR_UNSUPPORTED, PA_ERR_NULL, PA_ERR_ALIGN or PA_ERR_LAUNCH; nothing is
+ * launched for B == 0.
+ */
+int pa_rope_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, const float* cos_sin,
+                   int32_t max_pos, uint16_t* q_out, uint16_t* k_pool, uint16_t* v_pool,
+                   const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                   int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
+
+/*
  * pa_fill - write a run of consecutive tokens of every sequence into its pages
  * (prefill).  ([README] KV page pool item: prefill fills prompt pages, through
  * the same per-(sequence, layer) block table that decode reads.)

@@ -29,7 +29,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, f) for f in ("pa_api.cpp", "pa_sched.cpp", "pa_kernels.hip", "pa_prefill.hip")]
+    srcs = [os.path.join(CSRC, f) for f in ("pa_api.cpp", "pa_sched.cpp", "pa_kernels.hip", "pa_prefill.hip", "pa_rope.hip")]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-x", "hip", *srcs, "-o", tmp]

@@ -6,6 +6,7 @@
 
 #include "pa_kernels.h"
 #include "pa_prefill.h"
+#include "pa_rope.h"
 
 namespace {
 
@@ -127,6 +128,39 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
   if (pa::launch_append(k_new, v_new, k_pool, v_pool, block_table, max_blocks, seq_lens, B,
                         stream) != hipSuccess)
     return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
+int pa_rope_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, const float* cos_sin,
+                   int32_t max_pos, uint16_t* q_out, uint16_t* k_pool, uint16_t* v_pool,
+                   const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens, int32_t B,
+                   int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream) {
+  if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT || max_pos <= 0 ||
+      num_pages <= 0 || num_pages > INT32_MAX)
+    return PA_ERR_SHAPE;
+  const int dims = check_dims(Hq, Hkv, D);
+  if (dims != PA_OK) return dims;
+  if (B == 0) return PA_OK;
+  if (!q || !k_new || !v_new || !cos_sin || !q_out || !k_pool || !v_pool || !block_table || !seq_lens)
+    return PA_ERR_NULL;
+  if (misaligned(q) || misaligned(k_new) || misaligned(v_new) || misaligned(cos_sin) || misaligned(q_out) ||
+      misaligned(k_pool) || misaligned(v_pool))
+    return PA_ERR_ALIGN;
+  pa::RopeArgs a;
+  a.q = q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.cos_sin = cos_sin;
+  a.q_out = q_out;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.B = B;
+  a.max_blocks = max_blocks;
+  a.max_pos = max_pos;
+  a.num_pages = (int)num_pages;
+  if (pa::launch_rope_append(a, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 

@@ -20,7 +20,7 @@ PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN", -7: "PA_ERR_REJECTED",
           -8: "PA_ERR_BUDGET", -9: "PA_ERR_STATE"}
-EXPORTS = ("pa_status_string", "pa_append", "pa_fill", "pa_prefill", "pa_decode_workspace_bytes",
+EXPORTS = ("pa_status_string", "pa_append", "pa_rope_append", "pa_fill", "pa_prefill", "pa_decode_workspace_bytes",
            "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_merge",
            "pa_sched_budget_pages", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_admit",
            "pa_sched_grow", "pa_sched_block_table", "pa_sched_finish", "pa_sched_decode_batch",
@@ -49,6 +49,8 @@ def load() -> ctypes.CDLL:
     lib.pa_append.argtypes = [P, P, P, P, P, I32, P, I32, I32, I32, I64, P]
     lib.pa_append.restype = ctypes.c_int
     lib.pa_fill.argtypes = [P, P, P, P, P, I32, P, P, I32, I64, I32, I32, I64, P]
+    lib.pa_rope_append.argtypes = [P, P, P, P, I32, P, P, P, P, I32, P, I32, I32, I32, I32, I64, P]
+    lib.pa_rope_append.restype = ctypes.c_int
     lib.pa_fill.restype = ctypes.c_int
     lib.pa_prefill.argtypes = [P, P, P, P, I32, I64, I32, I32, I32, F32, I32, P, P]
     lib.pa_prefill.restype = ctypes.c_int
@@ -122,6 +124,24 @@ def pa_append(k_new, v_new, k_pool, v_pool, block_table, seq_lens, stream=None) 
                        block_table.shape[1], _ptr(seq_lens, torch.int32, "seq_lens"), B, Hkv, D,
                        k_pool.shape[0], _stream(k_pool.device, stream))
     _check("pa_append", st)
+
+
+def pa_rope_append(q, k_new, v_new, cos_sin, k_pool, v_pool, block_table, seq_lens, q_out=None,
+                   stream=None) -> torch.Tensor:
+    """RoPE of q and k_new at position seq_lens - 1 (cos_sin fp32 [max_pos][64]: 32 cosines then 32
+    sines), then the append of the rotated key and the value; returns q_out bf16 [B][32][64]."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    lib = load()
+    st = lib.pa_rope_append(_bf16(q, "q"), _bf16(k_new, "k_new"), _bf16(v_new, "v_new"),
+                            _ptr(cos_sin, torch.float32, "cos_sin"), cos_sin.shape[0], _bf16(q_out, "q_out"),
+                            _bf16(k_pool, "k_pool"), _bf16(v_pool, "v_pool"), _ptr(block_table, torch.int32, "block_table"),
+                            block_table.shape[1], _ptr(seq_lens, torch.int32, "seq_lens"), B, Hq, Hkv, D,
+                            k_pool.shape[0], _stream(q.device, stream))
+    _check("pa_rope_append", st)
+    return q_out
 
 
 def pa_fill(k_src, v_src, k_pool, v_pool, block_table, cu_tokens, start=None, stream=None) -> None:

@@ -291,6 +291,15 @@ def _layer_values(lay: Layout, l: int, n: int, c: int, dev) -> Tuple[torch.Tenso
             _randn_bf16((n, ROW_ELEMS), lay.sigma_v, dev, _torch_seed(lay.config_id, lay.draw, _S_V, (l << 16) | c)))
 
 
+def rope_table(max_pos: int = 2048, base: float = 500000.0, device="cpu") -> torch.Tensor:
+    """A RoPE table fp32 [max_pos][64] for the rotation's input: row p holds
+    cos(p w_i) for i < 32, then sin(p w_i), with w_i = base^(-2i/64), computed
+    in FP64.  (The pages give no base; 500000 is a synthetic choice.)"""
+    w = base ** (-torch.arange(32, dtype=torch.float64) * 2.0 / 64.0)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * w[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).to(torch.float32).to(device)
+
+
 def make_pools(lay: Layout, device="cpu", layers: Optional[List[int]] = None,
                chunk_rows: int = 1 << 22) -> Tuple[torch.Tensor, torch.Tensor]:
     """K and V planes, bf16 [num_pages][16][8][64], NaN everywhere except positions 0..L-2.

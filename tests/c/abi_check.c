@@ -21,6 +21,10 @@ int main(void) {
   printf("prefill_weights %d\n", pa_prefill(NULL, NULL, NULL, NULL, 4, 100, 32, 8, 64, 0.125f, 7, NULL, NULL));
   printf("prefill_empty %d\n", pa_prefill(NULL, NULL, NULL, NULL, 4, 0, 32, 8, 64, 0.125f, PA_PREFILL_WEIGHTS_FP16,
                                           NULL, NULL));
+  printf("rope_empty %d\n", pa_rope_append(NULL, NULL, NULL, NULL, 2048, NULL, NULL, NULL, NULL, 128, NULL, 0, 32, 8,
+                                            64, 1024, NULL));
+  printf("rope_table %d\n", pa_rope_append(NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL, 128, NULL, 4, 32, 8,
+                                            64, 1024, NULL));
   printf("fill_empty %d\n", pa_fill(NULL, NULL, NULL, NULL, NULL, 128, NULL, NULL, 0, 0, 8, 64, 1024, NULL));
 
   /* the scheduler: two requests that fit a 48-page pool, a third that waits

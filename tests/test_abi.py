@@ -241,3 +241,35 @@ def test_prefill_validation(lib):
     # nothing to do: no launch
     assert _prefill(lib, T=0) == 0
     assert _prefill(lib, T=0, q=None, out=None) == 0
+
+
+def _rope(lib, **kw):
+    args = dict(q=A, k_new=A, v_new=A, cs=A, max_pos=2048, q_out=A, k=A, v=A, bt=A, max_blocks=128, sl=A, B=4,
+                Hq=32, Hkv=8, D=64, num_pages=1024, stream=None)
+    args.update(kw)
+    return lib.pa_rope_append(args["q"], args["k_new"], args["v_new"], args["cs"], args["max_pos"], args["q_out"],
+                              args["k"], args["v"], args["bt"], args["max_blocks"], args["sl"], args["B"], args["Hq"],
+                              args["Hkv"], args["D"], args["num_pages"], args["stream"])
+
+
+def test_rope_append_validation(lib):
+    assert _rope(lib, B=-1) == -2
+    assert _rope(lib, B=4097) == -2
+    assert _rope(lib, max_pos=0) == -2
+    assert _rope(lib, max_blocks=0) == -2
+    assert _rope(lib, max_blocks=4097) == -2
+    assert _rope(lib, num_pages=0) == -2
+    assert _rope(lib, num_pages=1 << 31) == -2
+    assert _rope(lib, Hq=30) == -2
+    assert _rope(lib, Hkv=4, Hq=16) == -3
+    assert _rope(lib, D=128) == -3
+    assert _rope(lib, q=None) == -1
+    assert _rope(lib, cs=None) == -1
+    assert _rope(lib, q_out=None) == -1
+    assert _rope(lib, sl=None) == -1
+    assert _rope(lib, cs=MIS) == -6
+    assert _rope(lib, q_out=MIS) == -6
+    assert _rope(lib, v=MIS) == -6
+    # nothing to do: no launch
+    assert _rope(lib, B=0) == 0
+    assert _rope(lib, B=0, q=None, cs=None) == 0

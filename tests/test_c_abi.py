@@ -21,6 +21,8 @@ EXPECTED = {
     "prefill_weights": "-2",  # weights = 7 is neither mode: PA_ERR_SHAPE
     "prefill_empty": "0",     # T = 0: nothing to do
     "fill_empty": "0",        # B = 0: nothing to do
+    "rope_empty": "0",        # B = 0: nothing to do
+    "rope_table": "-2",       # max_pos = 0: no table row for any position (PA_ERR_SHAPE)
     # prompt 40 + 64 new - 1 = 103 tokens -> 7 pages x 16 layers
     "budget": "0 112",
     "create": "0",

@@ -134,3 +134,45 @@ def test_queued_decode_replays():
         other = ops.pa_decode(x["q"], k_pool, v_pool, bt, sl, lay.scale, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(other, eager)
+
+
+def test_rope_append_replays():
+    """RoPE + append captured in a graph: between replays the program's own eager
+    work overwrites the rotated queries and the appended slots; every replay
+    restores them bit for bit, equal to the eager call and to the oracle."""
+    from oracle.rope import rope_append_ref
+    lay = synth.small()
+    l = 2
+    k_pool, v_pool = synth.make_pools(lay, "cuda", layers=[l])
+    x = synth.step_inputs(lay, l, "cuda")
+    table = synth.rope_table(2048, device="cuda")
+    bt = torch.from_numpy(lay.block_tables[l]).cuda()
+    sl = torch.from_numpy(lay.seq_lens).cuda()
+    q_out = torch.empty_like(x["q"])
+    kp0, vp0 = synth.bits(k_pool), synth.bits(v_pool)
+
+    def step():
+        ops.pa_rope_append(x["q"], x["k_new"], x["v_new"], table, k_pool, v_pool, bt, sl, q_out=q_out)
+
+    step()
+    torch.cuda.synchronize()
+    eager_q, eager_k, eager_v = q_out.clone(), k_pool.clone(), v_pool.clone()
+    qr, kr, vr = rope_append_ref(synth.bits(x["q"]), synth.bits(x["k_new"]), synth.bits(x["v_new"]),
+                                 table.cpu().numpy(), kp0, vp0, lay.block_tables[l], lay.seq_lens,
+                                 np.zeros((lay.B, 32, 64), np.uint16))
+    assert np.array_equal(synth.bits(eager_q), qr)
+    assert np.array_equal(synth.bits(eager_k), kr) and np.array_equal(synth.bits(eager_v), vr)
+    g = capture(step)
+    junk_k = torch.full_like(x["k_new"], 3.0)
+    junk_v = torch.full_like(x["v_new"], -5.0)
+    for rep in range(3):
+        q_out.fill_(7.0)
+        ops.pa_append(junk_k, junk_v, k_pool, v_pool, bt, sl)  # clobbers every appended slot
+        torch.cuda.synchronize()
+        assert not torch.equal(k_pool.view(torch.int16), eager_k.view(torch.int16))
+        say(f"rope_append graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q_out.view(torch.int16), eager_q.view(torch.int16)), f"replay {rep}: q_out"
+        assert torch.equal(k_pool.view(torch.int16), eager_k.view(torch.int16)), f"replay {rep}: k_pool"
+        assert torch.equal(v_pool.view(torch.int16), eager_v.view(torch.int16)), f"replay {rep}: v_pool"

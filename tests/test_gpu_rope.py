@@ -1,0 +1,151 @@
+"""pa_rope_append on the GPU against oracle/rope.py, bit for bit.
+
+The rotation is specified as single FP32 operations with BF16 round-to-nearest,
+which the oracle takes in the same precision, so q_out and both pools must equal
+the oracle's exactly.  Cases: edge positions (0, a page's last and first slot,
+the table's last row), skipped sequences (empty, past the table, invalid page),
+an arbitrary table, in-place q, the headline workload's layer at full size
+(only the appended rows may change in the 4 GiB pools), and rotation followed
+by paged decode against the FP64 decode oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode_ref
+from oracle.rope import rope_append_ref
+from paged_kv_cache_205_amd import ops, synth
+from tests.helpers import check_close, say
+from tests.test_oracle_rope import _case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.load()
+
+
+def dev_bf16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out, in_place=False):
+    say(f"pa_rope_append B={q.shape[0]} max_pos={table.shape[0]} pages={k_pool.shape[0]} lens={lens.tolist()[:8]}")
+    qd = dev_bf16(q)
+    qo = qd if in_place else dev_bf16(q_out)
+    k, v = dev_bf16(k_pool), dev_bf16(v_pool)
+    ops.pa_rope_append(qd, dev_bf16(k_new), dev_bf16(v_new), torch.from_numpy(table).cuda(), k, v,
+                       torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda(), q_out=qo)
+    torch.cuda.synchronize()
+    return host_bits(qo), host_bits(k), host_bits(v)
+
+
+def test_edge_positions_and_skips_bit_exact():
+    q, k_new, v_new, table, k_pool, v_pool, bt, q_out = _case(5)
+    lens = np.array([1, 16, 17, 0, 64], np.int32)
+    bt[4, 3] = -1  # invalid page entry: skipped
+    want = rope_append_ref(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    got = run(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    for w, g, name in zip(want, got, ("q_out", "k_pool", "v_pool")):
+        assert np.array_equal(g, w), name
+
+
+def test_positions_past_the_table_are_skipped():
+    q, k_new, v_new, table, k_pool, v_pool, bt, q_out = _case(6, max_pos=20)
+    lens = np.array([21, 20, 3, 40, 5], np.int32)
+    want = rope_append_ref(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    got = run(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    for w, g, name in zip(want, got, ("q_out", "k_pool", "v_pool")):
+        assert np.array_equal(g, w), name
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_arbitrary_table_bit_exact(seed):
+    """Any FP32 table (not a rotation: mixed signs and magnitudes), many sequences."""
+    rng = np.random.default_rng(40 + seed)
+    B, max_blocks = 300, 8
+    num_pages = B * max_blocks
+    q, k_new, v_new, _, k_pool, v_pool, bt, q_out = _case(20 + seed, B=B, max_blocks=max_blocks, num_pages=num_pages)
+    table = (rng.standard_normal((128, 64)) * rng.choice([1e-3, 1.0, 30.0], size=(128, 64))).astype(np.float32)
+    lens = rng.integers(0, 129, size=B).astype(np.int32)
+    want = rope_append_ref(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    got = run(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    for w, g, name in zip(want, got, ("q_out", "k_pool", "v_pool")):
+        assert np.array_equal(g, w), name
+
+
+def test_in_place_query():
+    q, k_new, v_new, table, k_pool, v_pool, bt, q_out = _case(7)
+    lens = np.array([3, 9, 33, 50, 64], np.int32)
+    want = rope_append_ref(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out)
+    got = run(q, k_new, v_new, table, k_pool, v_pool, bt, lens, q_out, in_place=True)
+    for w, g, name in zip(want, got, ("q_out", "k_pool", "v_pool")):
+        assert np.array_equal(g, w), name
+
+
+def test_full_workload_layer():
+    """The headline workload's layer 0 (64 sequences at position 2047, 4 GiB pools):
+    q_out equals the oracle, the appended rows equal the oracle's, and nothing
+    else in the pools changes."""
+    lay = synth.full()
+    dev = "cuda"
+    k_pool, v_pool = synth.make_pools(lay, dev, layers=[0])
+    x = synth.step_inputs(lay, 0, dev)
+    table = synth.rope_table(2048, device=dev)
+    bt = torch.from_numpy(lay.block_tables[0]).to(dev)
+    sl = torch.from_numpy(lay.seq_lens).to(dev)
+    k0, v0 = k_pool.clone(), v_pool.clone()
+    say("pa_rope_append full workload layer 0")
+    q_out = ops.pa_rope_append(x["q"], x["k_new"], x["v_new"], table, k_pool, v_pool, bt, sl)
+    torch.cuda.synchronize()
+    pos = lay.seq_lens.astype(np.int64) - 1
+    pages = lay.block_tables[0][np.arange(lay.B), pos // 16]
+    slots = pos % 16
+    tcpu = table.cpu().numpy()
+    # the oracle on the touched rows only: a two-page pool holding the slots
+    for b in range(lay.B):
+        kp = np.zeros((1, 16, 8, 64), np.uint16)
+        vp = np.zeros((1, 16, 8, 64), np.uint16)
+        want = rope_append_ref(synth.bits(x["q"][b:b + 1]), synth.bits(x["k_new"][b:b + 1]),
+                               synth.bits(x["v_new"][b:b + 1]), tcpu, kp, vp,
+                               np.array([[0] * 127 + [0]], np.int32), np.array([lay.seq_lens[b]], np.int32),
+                               np.zeros((1, 32, 64), np.uint16))
+        assert np.array_equal(synth.bits(q_out[b:b + 1]), want[0]), f"q_out of sequence {b}"
+        assert np.array_equal(synth.bits(k_pool[pages[b], slots[b]]), want[1][0, slots[b]]), f"k row of sequence {b}"
+        assert np.array_equal(synth.bits(v_pool[pages[b], slots[b]]), want[2][0, slots[b]]), f"v row of sequence {b}"
+    # nothing else changed (NaN-safe bit comparison on the device)
+    touched = torch.zeros(k_pool.shape[:2], dtype=torch.bool, device=dev)
+    touched[torch.from_numpy(pages).to(dev), torch.from_numpy(slots).to(dev)] = True
+    for cur, old in ((k_pool, k0), (v_pool, v0)):
+        diff = (cur.view(torch.int16) != old.view(torch.int16)).flatten(2).any(dim=2)
+        assert not bool((diff & ~touched).any()), "a row outside the appended slots changed"
+
+
+def test_rotation_then_decode():
+    """Rotate and append on the small workload's layer, then decode with the rotated
+    queries: equal to the FP64 decode oracle over the oracle's rotated state."""
+    lay = synth.small()
+    dev = "cuda"
+    k_pool, v_pool = synth.make_pools(lay, dev, layers=[0])
+    x = synth.step_inputs(lay, 0, dev)
+    table = synth.rope_table(2048, device=dev)
+    bt = torch.from_numpy(lay.block_tables[0]).to(dev)
+    sl = torch.from_numpy(lay.seq_lens).to(dev)
+    kp0, vp0 = synth.bits(k_pool), synth.bits(v_pool)
+    say("pa_rope_append + pa_decode small workload layer 0")
+    q_out = ops.pa_rope_append(x["q"], x["k_new"], x["v_new"], table, k_pool, v_pool, bt, sl)
+    out = ops.pa_decode(q_out, k_pool, v_pool, bt, sl, lay.scale).cpu().numpy()
+    qr, k2, v2 = rope_append_ref(synth.bits(x["q"]), synth.bits(x["k_new"]), synth.bits(x["v_new"]),
+                                 table.cpu().numpy(), kp0, vp0, lay.block_tables[0], lay.seq_lens,
+                                 np.zeros((lay.B, 32, 64), np.uint16))
+    assert np.array_equal(synth.bits(q_out), qr)
+    assert np.array_equal(synth.bits(k_pool), k2) and np.array_equal(synth.bits(v_pool), v2)
+    ref = decode_ref(qr, k2, v2, lay.block_tables[0], lay.seq_lens, lay.scale)
+    check_close(out, ref, "decode after rope_append")
