@@ -691,6 +691,26 @@ def main():
     torch.cuda.synchronize()
     ms_step_sep = t0.elapsed_time(t1) / args.steps
 
+    # the same step with RoPE of q and the new key at position L-1 fused into
+    # the launch (pa_rope_append_decode); the next steps append the plain rows again
+    table = synth.rope_table(lay.max_blocks * 16, device=dev)
+
+    def step_rope():
+        for l in range(lay.n_layers):
+            x = inputs[l]
+            ops.pa_rope_append_decode(x["k_new"], x["v_new"], k_pool, v_pool, x["q"], table, bt[l], seq_lens,
+                                      lay.scale, out=outs[l], partition_tokens=part, workspace=ws)
+
+    for _ in range(args.warmup):
+        step_rope()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step_rope()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step_rope = t0.elapsed_time(t1) / args.steps
+
     # decode launches timed one by one (separate pass, same work)
     dec_ms = []
     for _ in range(args.steps):
@@ -776,6 +796,7 @@ def main():
                              "min": round(float(np.min(step_ms)) * 1e3, 2),
                              "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2)},
         "us_per_step_separate_append_decode": round(ms_step_sep * 1e3, 2),
+        "us_per_step_rope_append_decode": round(ms_step_rope * 1e3, 2),
         "seq_steps_per_s": round(lay.B / (best_ms * 1e-3), 1),
         "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "stream_read_GBps": None if stream_gbs is None else round(stream_gbs, 1),

@@ -145,6 +145,27 @@ int pa_rope_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_n
                    int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, hipStream_t stream);
 
 /*
+ * pa_rope_append_decode - pa_rope_append and pa_decode in one launch: q and
+ * the new key are rotated by RoPE at position L-1 exactly as pa_rope_append
+ * rotates them, the rotated key and the value are appended, and the attention
+ * runs with the rotated query.  The pools and out are bit-identical to
+ * pa_rope_append followed by pa_decode on its q_out (the rotated q itself is
+ * not stored).  ([README] feature list and KV page pool item, as for
+ * pa_rope_append; [README] paged decode attention item, as for pa_decode.)
+ *
+ * Arguments as pa_append_decode, plus cos_sin fp32 [max_pos][D] as for
+ * pa_rope_append, with max_pos >= 16 * max_blocks so that the table covers
+ * every position the block table can address (else PA_ERR_SHAPE).  Unlike
+ * pa_rope_append it skips nothing: every sequence is decoded as pa_decode
+ * decodes it.
+ */
+int pa_rope_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
+                          const uint16_t* q, const float* cos_sin, int32_t max_pos, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
+                          int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pa_fill - write a run of consecutive tokens of every sequence into its pages
  * (prefill).  ([README] KV page pool item: prefill fills prompt pages, through
  * the same per-(sequence, layer) block table that decode reads.)

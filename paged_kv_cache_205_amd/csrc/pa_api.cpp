@@ -235,7 +235,8 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
                float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
                int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool_w, uint16_t* v_pool_w,
-               bool fused_append, hipStream_t stream) {
+               bool fused_append, const float* cos_sin, int32_t max_pos, hipStream_t stream) {
+  const bool rope = cos_sin != nullptr || max_pos != 0;
   if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT ||
       num_pages <= 0 || num_pages > INT32_MAX || !isfinite(scale))
     return PA_ERR_SHAPE;
@@ -250,6 +251,11 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   if (misaligned(q) || misaligned(k_pool) || misaligned(v_pool) || misaligned(out))
     return PA_ERR_ALIGN;
   if (fused_append && (misaligned(k_new) || misaligned(v_new))) return PA_ERR_ALIGN;
+  if (rope) {  // the table covers every position the block table can address
+    if ((int64_t)max_pos < (int64_t)max_blocks * pa::kPageTokens) return PA_ERR_SHAPE;
+    if (!cos_sin) return PA_ERR_NULL;
+    if (misaligned(cos_sin)) return PA_ERR_ALIGN;
+  }
   if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
   if (misaligned(workspace)) return PA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
@@ -282,7 +288,9 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.narrow = device_cus();
   // the kernel uses the queue only when the plan has more items than the grid
   a.queue = reinterpret_cast<int*>(ws + plan.off_q);
-  if (pa::launch_decode(a, grid, fused_append, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  a.cos_sin = cos_sin;
+  a.max_pos = max_pos;
+  if (pa::launch_decode(a, grid, fused_append, rope, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 
@@ -297,7 +305,7 @@ int pa_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
               hipStream_t stream) {
   return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D,
                     num_pages, partition_tokens, workspace, workspace_bytes, nullptr, nullptr,
-                    nullptr, nullptr, false, stream);
+                    nullptr, nullptr, false, nullptr, 0, stream);
 }
 
 int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
@@ -307,7 +315,18 @@ int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_p
                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D,
                     num_pages, partition_tokens, workspace, workspace_bytes, k_new, v_new, k_pool,
-                    v_pool, true, stream);
+                    v_pool, true, nullptr, 0, stream);
+}
+
+int pa_rope_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, uint16_t* v_pool,
+                          const uint16_t* q, const float* cos_sin, int32_t max_pos, const int32_t* block_table,
+                          int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
+                          int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (max_pos <= 0) return PA_ERR_SHAPE;
+  return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D,
+                    num_pages, partition_tokens, workspace, workspace_bytes, k_new, v_new, k_pool,
+                    v_pool, true, cos_sin, max_pos, stream);
 }
 
 int pa_merge(const float* part_o, const float* part_m, const float* part_l,

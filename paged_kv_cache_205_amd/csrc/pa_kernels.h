@@ -45,6 +45,8 @@ struct DecodeArgs {
   float* part_o;  // [B][Hq][S][D]
   float* part_m;  // [B][Hq][S]
   float* part_l;  // [B][Hq][S]
+  const float* cos_sin;  // fused RoPE only: [max_pos][D], 32 cosines then 32 sines per position
+  int max_pos;           // rows of cos_sin (positions past it read its last row; the host requires >= 16 max_blocks)
 };
 
 struct MergeArgs {
@@ -75,6 +77,28 @@ struct FillArgs {
 
 hipError_t launch_fill(const FillArgs& a, hipStream_t stream);
 
+// RoPE arithmetic shared by the RoPE kernels.  One output of a rotation pair
+// (i, i + 32): x c - y s for the first half (second = false), x c + y s for the
+// second, each product and the sum a single FP32 operation rounded to nearest
+// (no fused multiply-add).
+__device__ __forceinline__ float rope_term(float x, float y, float c, float s, bool second) {
+#pragma clang fp contract(off)
+  const float a = x * c;
+  const float b = y * s;
+  return second ? a + b : a - b;
+}
+// FP32 -> BF16 bits, to nearest with ties to even; a NaN keeps its sign and
+// upper payload with the quiet bit set.
+__device__ __forceinline__ unsigned bf16_rne(float f) {
+  const unsigned u = __builtin_bit_cast(unsigned, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// BF16 element e (0 or 1) of a dword, as FP32.
+__device__ __forceinline__ float bf16_lo_hi(unsigned w, int e) {
+  return __builtin_bit_cast(float, e == 0 ? w << 16 : w & 0xffff0000u);
+}
+
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,
                          const int32_t* seq_lens, int B, hipStream_t stream);
@@ -83,7 +107,8 @@ size_t decode_lds_bytes(int B);
 // (all with the same page count), and its smallest split for a batch of B sequences.
 int auto_split_pages(long long total_pages, int B);
 int auto_split_min_pages(int B);
-hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream);
+// rope: also rotate q and the new key by RoPE at position L-1 (needs fused_append).
+hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, bool rope, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 
 }  // namespace pa

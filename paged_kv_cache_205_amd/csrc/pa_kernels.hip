@@ -204,7 +204,7 @@ struct ItemPrefetch {
   u32x4 row;  // appended K (lanes 0-7) / V (lanes 8-15) row of the wave's head
 };
 
-template <bool kAppend>
+template <bool kAppend, bool kRope>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, int nsplit, int L, int n,
                                             const ItemPrefetch& pre, bool primed, DmaOffsets doff,
                                             unsigned char (*ring)[kRing][kSlotBytes], int* last_split) {
@@ -266,6 +266,29 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
       if (lane < 16) {
         const size_t head_off = ((size_t)b * kKvHeads + g) * kHeadDim + 8 * (lane & 7);
         new_row = prefetched ? pre.row : ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
+      }
+      if (kRope) {
+        // RoPE of the new key at position L-1: lane j < 8 holds dims 8j..8j+7,
+        // whose rotation partners (32 dims away) lane j ^ 4 holds.  Every lane
+        // takes part in the swap; lanes 8-15 keep the value row.
+        u32x4 y;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) y[m] = (unsigned)__shfl_xor((int)new_row[m], 4);
+        const float* cs = a.cos_sin + (size_t)min(L - 1, a.max_pos - 1) * kHeadDim + 8 * (lane & 3);
+        const bool second = (lane & 4) != 0;
+        u32x4 r;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          unsigned o[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            o[e] = bf16_rne(rope_term(bf16_lo_hi(new_row[m], e), bf16_lo_hi(y[m], e), cs[2 * m + e],
+                                      cs[32 + 2 * m + e], second));
+          r[m] = o[0] | (o[1] << 16);
+        }
+        if (lane < 8) new_row = r;
+      }
+      if (lane < 16) {
         const size_t dst = ((size_t)(uint32_t)page_of(k_app) * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
         *reinterpret_cast<u32x4*>((lane < 8 ? a.k_pool_w : a.v_pool_w) + dst) = new_row;
       }
@@ -274,8 +297,30 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 
   // B operand of S^T = K Q^T: query head 4g + (t % 4), dims 8c..8c+7 and 32+8c..32+8c+7.
   const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
-  const bf16x8 qb0 = __builtin_bit_cast(bf16x8, prefetched ? pre.q0 : ld16(qrow + 8 * c));
-  const bf16x8 qb1 = __builtin_bit_cast(bf16x8, prefetched ? pre.q1 : ld16(qrow + 32 + 8 * c));
+  bf16x8 qb0 = __builtin_bit_cast(bf16x8, prefetched ? pre.q0 : ld16(qrow + 8 * c));
+  bf16x8 qb1 = __builtin_bit_cast(bf16x8, prefetched ? pre.q1 : ld16(qrow + 32 + 8 * c));
+  if (kRope) {
+    // RoPE of the query at position L-1: the lane's two chunks, dims 8c.. and
+    // 32 + 8c.., are 8 rotation pairs of one head.
+    const float* cs = a.cos_sin + (size_t)min(L - 1, a.max_pos - 1) * kHeadDim + 8 * c;
+    const u32x4 x0 = __builtin_bit_cast(u32x4, qb0), x1 = __builtin_bit_cast(u32x4, qb1);
+    u32x4 r0, r1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      unsigned o0[2], o1[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float lo = bf16_lo_hi(x0[m], e), hi = bf16_lo_hi(x1[m], e);
+        const float cf = cs[2 * m + e], sf = cs[32 + 2 * m + e];
+        o0[e] = bf16_rne(rope_term(lo, hi, cf, sf, false));
+        o1[e] = bf16_rne(rope_term(hi, lo, cf, sf, true));
+      }
+      r0[m] = o0[0] | (o0[1] << 16);
+      r1[m] = o1[0] | (o1[1] << 16);
+    }
+    qb0 = __builtin_bit_cast(bf16x8, r0);
+    qb1 = __builtin_bit_cast(bf16x8, r1);
+  }
 
   auto issue = [&](int slot, int32_t page) { issue_page(a, ring[g][slot], page, doff); };
   // LDS read offsets: K (A operand) token t, chunks c and 4+c; V^T element
@@ -771,7 +816,7 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
   return p;
 }
 
-template <bool kAppend>
+template <bool kAppend, bool kRope>
 __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   // Dynamic LDS: the page ring, then the plan's per-sequence arrays.
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -885,7 +930,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   // work.  Nothing of the plan is kept in registers across an item: the next
   // item is derived from the plan in LDS.
   while (b >= 0) {
-    if (s < nsplit) decode_item<kAppend>(a, b, s, nsplit, L, n, pre, primed, doff, ring, &last_split);
+    if (s < nsplit) decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, primed, doff, ring, &last_split);
     pre.b = -1;
     primed = false;
     b = -1;
@@ -1001,7 +1046,7 @@ int auto_split_min_pages(int B) { return auto_min_pages(B); }
 // once per device (the attribute belongs to the device the call is made on).
 static hipError_t allow_decode_lds(const void* kernel, int which) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> done[2][kMaxDevices];
+  static std::atomic<int> done[3][kMaxDevices];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
@@ -1012,18 +1057,20 @@ static hipError_t allow_decode_lds(const void* kernel, int which) {
   return err;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, hipStream_t stream) {
-  const size_t lds = decode_dynamic_lds_bytes(a.B);
-  if (fused_append) {
-    const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<true>), 1);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
-  } else {
-    const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<false>), 0);
-    if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(64 * kKvHeads), lds, stream, a);
-  }
+template <bool kAppend, bool kRope>
+static hipError_t launch_decode_variant(const DecodeArgs& a, int grid, int which, hipStream_t stream) {
+  const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<kAppend, kRope>), which);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((decode_kernel<kAppend, kRope>), dim3(grid), dim3(64 * kKvHeads), decode_dynamic_lds_bytes(a.B),
+                     stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, bool rope, hipStream_t stream) {
+  if (rope && !fused_append) return hipErrorInvalidValue;
+  if (rope) return launch_decode_variant<true, true>(a, grid, 2, stream);
+  if (fused_append) return launch_decode_variant<true, false>(a, grid, 1, stream);
+  return launch_decode_variant<false, false>(a, grid, 0, stream);
 }
 
 hipError_t launch_fill(const FillArgs& a, hipStream_t stream) {

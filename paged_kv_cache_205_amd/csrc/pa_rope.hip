@@ -12,8 +12,8 @@
 // in it), and dimension i turns with dimension i + 32:
 //   x'[i]      = x[i] c_i - x[i + 32] s_i
 //   x'[i + 32] = x[i + 32] c_i + x[i] s_i
-// Each product and the sum are single FP32 operations (contraction is off in
-// rotate_chunk), rounded to BF16 to nearest, ties to even, by integer ops.
+// Each product and the sum are single FP32 operations (rope_term, with
+// contraction off), rounded to BF16 to nearest, ties to even, by integer ops.
 //
 // Work: one wave per sequence.  A 64-wide BF16 head row is 128 bytes, 8 lanes
 // of 16 bytes: lane l holds chunk j = l % 8 (dims 8j .. 8j + 7) of row l / 8,
@@ -38,31 +38,17 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// FP32 -> BF16 bits, to nearest with ties to even; a NaN keeps its sign and
-// upper payload with the quiet bit set.
-__device__ __forceinline__ unsigned bf16_rne(float f) {
-  const unsigned u = __builtin_bit_cast(unsigned, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
 // One 16-byte chunk (8 BF16 values) rotated: x is the lane's chunk, y its
 // partner's; the first half of a row takes x c - y s, the second x c + y s.
 __device__ __forceinline__ u32x4 rotate_chunk(u32x4 x, u32x4 y, const float (&c)[8], const float (&s)[8],
                                               bool second) {
-#pragma clang fp contract(off)
   u32x4 r;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const float xv[2] = {__builtin_bit_cast(float, x[m] << 16), __builtin_bit_cast(float, x[m] & 0xffff0000u)};
-    const float yv[2] = {__builtin_bit_cast(float, y[m] << 16), __builtin_bit_cast(float, y[m] & 0xffff0000u)};
     unsigned o[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const float a = xv[e] * c[2 * m + e];
-      const float b = yv[e] * s[2 * m + e];
-      o[e] = bf16_rne(second ? a + b : a - b);
-    }
+    for (int e = 0; e < 2; ++e)
+      o[e] = bf16_rne(rope_term(bf16_lo_hi(x[m], e), bf16_lo_hi(y[m], e), c[2 * m + e], s[2 * m + e], second));
     r[m] = o[0] | (o[1] << 16);
   }
   return r;

@@ -273,3 +273,25 @@ def test_rope_append_validation(lib):
     # nothing to do: no launch
     assert _rope(lib, B=0) == 0
     assert _rope(lib, B=0, q=None, cs=None) == 0
+
+
+def _rope_decode(lib, **kw):
+    args = dict(k_new=A, v_new=A, k=A, v=A, q=A, cs=A, max_pos=2048, bt=A, max_blocks=128, sl=A, scale=0.125, out=A,
+                B=4, Hq=32, Hkv=8, D=64, num_pages=1024, part=0, ws=A, ws_n=1 << 30, stream=None)
+    args.update(kw)
+    return lib.pa_rope_append_decode(args["k_new"], args["v_new"], args["k"], args["v"], args["q"], args["cs"],
+                                     args["max_pos"], args["bt"], args["max_blocks"], args["sl"], args["scale"],
+                                     args["out"], args["B"], args["Hq"], args["Hkv"], args["D"], args["num_pages"],
+                                     args["part"], args["ws"], args["ws_n"], args["stream"])
+
+
+def test_rope_append_decode_validation(lib):
+    assert _rope_decode(lib, max_pos=0) == -2
+    assert _rope_decode(lib, max_pos=2047) == -2  # the table must cover 16 x 128 positions
+    assert _rope_decode(lib, max_pos=64, max_blocks=5) == -2
+    assert _rope_decode(lib, cs=None) == -1
+    assert _rope_decode(lib, cs=MIS) == -6
+    assert _rope_decode(lib, k_new=None) == -1
+    assert _rope_decode(lib, Hq=16, Hkv=4) == -3
+    assert _rope_decode(lib, ws=None) == -4
+    assert _rope_decode(lib, B=0) == 0  # nothing to do: no launch

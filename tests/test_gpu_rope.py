@@ -6,7 +6,9 @@ the oracle's exactly.  Cases: edge positions (0, a page's last and first slot,
 the table's last row), skipped sequences (empty, past the table, invalid page),
 an arbitrary table, in-place q, the headline workload's layer at full size
 (only the appended rows may change in the 4 GiB pools), and rotation followed
-by paged decode against the FP64 decode oracle.
+by paged decode against the FP64 decode oracle.  The fused pa_rope_append_decode
+must leave the pools and the output bit-identical to pa_rope_append followed by
+pa_decode (uniform, queued and fixed-split plans).
 """
 import numpy as np
 import pytest
@@ -149,3 +151,38 @@ def test_rotation_then_decode():
     assert np.array_equal(synth.bits(k_pool), k2) and np.array_equal(synth.bits(v_pool), v2)
     ref = decode_ref(qr, k2, v2, lay.block_tables[0], lay.seq_lens, lay.scale)
     check_close(out, ref, "decode after rope_append")
+
+
+@pytest.mark.parametrize("name,partition", [("small", 0), ("skewed", 0), ("fragmented", 64), ("full", 0)])
+def test_fused_rope_decode_equals_separate_calls(name, partition):
+    """pa_rope_append_decode leaves the pools and out bit-identical to pa_rope_append
+    followed by pa_decode on its rotated queries (uniform, queued and fixed-split
+    plans); on the small workload both also match the oracles."""
+    lay = synth.get(name)
+    dev = "cuda"
+    l = 1 if lay.n_layers > 1 else 0
+    x = synth.step_inputs(lay, l, dev)
+    table = synth.rope_table(2048, device=dev)
+    bt = torch.from_numpy(lay.block_tables[l]).to(dev)
+    sl = torch.from_numpy(lay.seq_lens).to(dev)
+    say(f"fused rope decode {name} B={lay.B} partition={partition}")
+    k1, v1 = synth.make_pools(lay, dev, layers=[l])
+    host = (synth.bits(k1), synth.bits(v1)) if name == "small" else None
+    q_rot = ops.pa_rope_append(x["q"], x["k_new"], x["v_new"], table, k1, v1, bt, sl)
+    out1 = ops.pa_decode(q_rot, k1, v1, bt, sl, lay.scale, partition_tokens=partition)
+    k2, v2 = synth.make_pools(lay, dev, layers=[l])
+    out2 = ops.pa_rope_append_decode(x["k_new"], x["v_new"], k2, v2, x["q"], table, bt, sl, lay.scale,
+                                     partition_tokens=partition)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2), "out differs from the separate calls"
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), "k_pool differs"
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), "v_pool differs"
+    if host is not None:
+        qr, kr, vr = rope_append_ref(synth.bits(x["q"]), synth.bits(x["k_new"]), synth.bits(x["v_new"]),
+                                     table.cpu().numpy(), host[0], host[1], lay.block_tables[l], lay.seq_lens,
+                                     np.zeros((lay.B, 32, 64), np.uint16))
+        assert np.array_equal(synth.bits(k2), kr) and np.array_equal(synth.bits(v2), vr)
+        ref = decode_ref(qr, kr, vr, lay.block_tables[l], lay.seq_lens, lay.scale)
+        check_close(out2.cpu().numpy(), ref, "fused rope decode")
+    del k1, v1, k2, v2
+    torch.cuda.empty_cache()
