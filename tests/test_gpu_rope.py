@@ -186,3 +186,62 @@ def test_fused_rope_decode_equals_separate_calls(name, partition):
         check_close(out2.cpu().numpy(), ref, "fused rope decode")
     del k1, v1, k2, v2
     torch.cuda.empty_cache()
+
+
+def test_fused_rope_decode_long_tables():
+    """Tables of 300 entries (the kernel reads each split's own entries, not the
+    whole row) with lengths up to 4800: fused equals the two calls bit for bit,
+    under the automatic and a fixed split."""
+    rng = np.random.default_rng(77)
+    B, max_blocks = 6, 300
+    num_pages = B * max_blocks + 5
+    q, k_new, v_new, _, k_pool, v_pool, bt, _ = _case(30, B=B, max_blocks=max_blocks, num_pages=num_pages)
+    lens = np.array([1, 17, 2048, 4095, 4800, 0], np.int32)
+    table = rng.standard_normal((16 * max_blocks, 64)).astype(np.float32)
+    dev_t = torch.from_numpy(table).cuda()
+    btd, sl = torch.from_numpy(bt).cuda(), torch.from_numpy(lens).cuda()
+    for part in (0, 256):
+        say(f"fused rope decode, 300-entry tables, partition {part}")
+        k1, v1 = dev_bf16(k_pool), dev_bf16(v_pool)
+        q_rot = ops.pa_rope_append(dev_bf16(q), dev_bf16(k_new), dev_bf16(v_new), dev_t, k1, v1, btd, sl)
+        out1 = ops.pa_decode(q_rot, k1, v1, btd, sl, 0.125, partition_tokens=part)
+        k2, v2 = dev_bf16(k_pool), dev_bf16(v_pool)
+        out2 = ops.pa_rope_append_decode(dev_bf16(k_new), dev_bf16(v_new), k2, v2, dev_bf16(q), dev_t, btd, sl, 0.125,
+                                         partition_tokens=part)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out2).all()
+        assert torch.equal(out1, out2) and torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+        assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+
+
+def test_fused_rope_decode_graph_replays():
+    """The fused call captured in a graph: eager work clobbers the appended slots and
+    the output between replays; every replay restores the eager result bit for bit."""
+    from tests.test_gpu_graph import capture
+    lay = synth.small()
+    l = 3
+    k_pool, v_pool = synth.make_pools(lay, "cuda", layers=[l])
+    x = synth.step_inputs(lay, l, "cuda")
+    table = synth.rope_table(2048, device="cuda")
+    bt = torch.from_numpy(lay.block_tables[l]).cuda()
+    sl = torch.from_numpy(lay.seq_lens).cuda()
+    ws = ops.workspace_for(lay.B, lay.max_blocks)
+    out = torch.empty((lay.B, 32, 64), device="cuda")
+
+    def step():
+        ops.pa_rope_append_decode(x["k_new"], x["v_new"], k_pool, v_pool, x["q"], table, bt, sl, lay.scale, out=out,
+                                  workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager_out, eager_k = out.clone(), k_pool.clone()
+    g = capture(step)
+    for rep in range(3):
+        out.fill_(-1.0)
+        ops.pa_append(torch.full_like(x["k_new"], 2.0), x["v_new"], k_pool, v_pool, bt, sl)
+        torch.cuda.synchronize()
+        say(f"fused rope decode graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), f"replay {rep}: out"
+        assert torch.equal(k_pool.view(torch.int16), eager_k.view(torch.int16)), f"replay {rep}: k_pool"
