@@ -263,27 +263,38 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
     if (pa % nsplit == s) {
       k_app = pa / nsplit;
       tau_app = (L - 1) % kPageTokens;
+      // RoPE of the new key at position L-1 (kRope): the table row is loaded
+      // beside the key row, so that both arrive in one round trip.
+      f32x4 kc0, kc1, ks0, ks1;
+      if (kRope) {
+        const float* cs = a.cos_sin + (size_t)min(L - 1, a.max_pos - 1) * kHeadDim + 8 * (lane & 3);
+        kc0 = *reinterpret_cast<const f32x4*>(cs);
+        kc1 = *reinterpret_cast<const f32x4*>(cs + 4);
+        ks0 = *reinterpret_cast<const f32x4*>(cs + 32);
+        ks1 = *reinterpret_cast<const f32x4*>(cs + 36);
+      }
       if (lane < 16) {
         const size_t head_off = ((size_t)b * kKvHeads + g) * kHeadDim + 8 * (lane & 7);
         new_row = prefetched ? pre.row : ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
       }
       if (kRope) {
-        // RoPE of the new key at position L-1: lane j < 8 holds dims 8j..8j+7,
-        // whose rotation partners (32 dims away) lane j ^ 4 holds.  Every lane
-        // takes part in the swap; lanes 8-15 keep the value row.
+        // Lane j < 8 holds dims 8j..8j+7, whose rotation partners (32 dims
+        // away) lane j ^ 4 holds.  Every lane takes part in the swap; lanes
+        // 8-15 keep the value row.
         u32x4 y;
 #pragma unroll
         for (int m = 0; m < 4; ++m) y[m] = (unsigned)__shfl_xor((int)new_row[m], 4);
-        const float* cs = a.cos_sin + (size_t)min(L - 1, a.max_pos - 1) * kHeadDim + 8 * (lane & 3);
         const bool second = (lane & 4) != 0;
+        const float cv[8] = {kc0[0], kc0[1], kc0[2], kc0[3], kc1[0], kc1[1], kc1[2], kc1[3]};
+        const float sv[8] = {ks0[0], ks0[1], ks0[2], ks0[3], ks1[0], ks1[1], ks1[2], ks1[3]};
         u32x4 r;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           unsigned o[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            o[e] = bf16_rne(rope_term(bf16_lo_hi(new_row[m], e), bf16_lo_hi(y[m], e), cs[2 * m + e],
-                                      cs[32 + 2 * m + e], second));
+            o[e] = bf16_rne(rope_term(bf16_lo_hi(new_row[m], e), bf16_lo_hi(y[m], e), cv[2 * m + e], sv[2 * m + e],
+                                      second));
           r[m] = o[0] | (o[1] << 16);
         }
         if (lane < 8) new_row = r;
@@ -299,27 +310,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   const uint16_t* qrow = a.q + ((size_t)b * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
   bf16x8 qb0 = __builtin_bit_cast(bf16x8, prefetched ? pre.q0 : ld16(qrow + 8 * c));
   bf16x8 qb1 = __builtin_bit_cast(bf16x8, prefetched ? pre.q1 : ld16(qrow + 32 + 8 * c));
+  // RoPE of the query at position L-1 (kRope): the lane's two chunks, dims
+  // 8c.. and 32 + 8c.., are 8 rotation pairs of one head.  The table row is
+  // loaded here beside q; the rotation waits until the item's first page
+  // copies are on their way.
+  f32x4 qc0, qc1, qs0, qs1;
   if (kRope) {
-    // RoPE of the query at position L-1: the lane's two chunks, dims 8c.. and
-    // 32 + 8c.., are 8 rotation pairs of one head.
     const float* cs = a.cos_sin + (size_t)min(L - 1, a.max_pos - 1) * kHeadDim + 8 * c;
-    const u32x4 x0 = __builtin_bit_cast(u32x4, qb0), x1 = __builtin_bit_cast(u32x4, qb1);
-    u32x4 r0, r1;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      unsigned o0[2], o1[2];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const float lo = bf16_lo_hi(x0[m], e), hi = bf16_lo_hi(x1[m], e);
-        const float cf = cs[2 * m + e], sf = cs[32 + 2 * m + e];
-        o0[e] = bf16_rne(rope_term(lo, hi, cf, sf, false));
-        o1[e] = bf16_rne(rope_term(hi, lo, cf, sf, true));
-      }
-      r0[m] = o0[0] | (o0[1] << 16);
-      r1[m] = o1[0] | (o1[1] << 16);
-    }
-    qb0 = __builtin_bit_cast(bf16x8, r0);
-    qb1 = __builtin_bit_cast(bf16x8, r1);
+    qc0 = *reinterpret_cast<const f32x4*>(cs);
+    qc1 = *reinterpret_cast<const f32x4*>(cs + 4);
+    qs0 = *reinterpret_cast<const f32x4*>(cs + 32);
+    qs1 = *reinterpret_cast<const f32x4*>(cs + 36);
   }
 
   auto issue = [&](int slot, int32_t page) { issue_page(a, ring[g][slot], page, doff); };
@@ -346,6 +347,26 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 #pragma unroll
     for (int u = 0; u < kRing; ++u)
       if (u < n) issue(u, page_of(u));
+  }
+  if (kRope) {
+    const u32x4 x0 = __builtin_bit_cast(u32x4, qb0), x1 = __builtin_bit_cast(u32x4, qb1);
+    const float cv[8] = {qc0[0], qc0[1], qc0[2], qc0[3], qc1[0], qc1[1], qc1[2], qc1[3]};
+    const float sv[8] = {qs0[0], qs0[1], qs0[2], qs0[3], qs1[0], qs1[1], qs1[2], qs1[3]};
+    u32x4 r0, r1;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      unsigned o0[2], o1[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float lo = bf16_lo_hi(x0[m], e), hi = bf16_lo_hi(x1[m], e);
+        o0[e] = bf16_rne(rope_term(lo, hi, cv[2 * m + e], sv[2 * m + e], false));
+        o1[e] = bf16_rne(rope_term(hi, lo, cv[2 * m + e], sv[2 * m + e], true));
+      }
+      r0[m] = o0[0] | (o0[1] << 16);
+      r1[m] = o1[0] | (o1[1] << 16);
+    }
+    qb0 = __builtin_bit_cast(bf16x8, r0);
+    qb1 = __builtin_bit_cast(bf16x8, r1);
   }
 
   for (int kb = 0; kb < n; kb += kRing) {
@@ -525,7 +546,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 // Work plan.  Every workgroup builds the same plan in LDS from seq_lens:
 //   pp      pages per split: a.part_pages if set, else ceil(total pages / n)
 //           clamped to [m, 128], n = 192 when every sequence has the same page
-//           count and 512 for mixed lengths (about n items), m = 4 for batches
+//           count and 384 for mixed lengths (about n items), m = 4 for batches
 //           of at most 64 sequences and 8 above;
 //   nsplit  ceil(npages / pp) splits per sequence (1 for an empty sequence);
 //   items   first every split of the multi-split sequences (sequence-major),
@@ -542,7 +563,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 
 constexpr int kTargetItems = 192;          // batches with one page count (and the host's guess)
 constexpr int kLongItemPages = 8;          // items averaging this many pages run one workgroup per CU
-constexpr int kTargetItemsMixed = 512;     // batches of mixed lengths (the queue takes what the active workgroups do not)
+constexpr int kTargetItemsMixed = 384;     // batches of mixed lengths (the queue takes what the active workgroups do not)
 constexpr int kAutoMinPages = 8;
 constexpr int kMaxSplitPages = 128;
 // Length buckets for handing out single-split items longest first: bucket k
@@ -680,7 +701,7 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     all_min_c = max(all_min_c, pl->wave_min[v]);
   }
   // One page count for every sequence: about 192 items, which suits streaming
-  // whole pages with one item per workgroup.  Mixed lengths: about 512 smaller
+  // whole pages with one item per workgroup.  Mixed lengths: about 384 smaller
   // items, so that long sequences are not left to a few workgroups at the end.
   const bool uniform = kPageCap - all_min_c == all_max;
   const int pp = part_pages > 0 ? part_pages
