@@ -258,6 +258,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   int k_app = -1;
   int tau_app = 0;
   u32x4 new_row = {0u, 0u, 0u, 0u};
+  f32x4 kc0, kc1, ks0, ks1;  // kRope: the table row of the new key's lanes
   if (kAppend) {
     const int pa = (L - 1) / kPageTokens;
     if (pa % nsplit == s) {
@@ -265,7 +266,6 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
       tau_app = (L - 1) % kPageTokens;
       // RoPE of the new key at position L-1 (kRope): the table row is loaded
       // beside the key row, so that both arrive in one round trip.
-      f32x4 kc0, kc1, ks0, ks1;
       if (kRope) {
         const float* cs = a.cos_sin + (size_t)min(L - 1, a.max_pos - 1) * kHeadDim + 8 * (lane & 3);
         kc0 = *reinterpret_cast<const f32x4*>(cs);
@@ -277,29 +277,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
         const size_t head_off = ((size_t)b * kKvHeads + g) * kHeadDim + 8 * (lane & 7);
         new_row = prefetched ? pre.row : ld16((lane < 8 ? a.k_new : a.v_new) + head_off);
       }
-      if (kRope) {
-        // Lane j < 8 holds dims 8j..8j+7, whose rotation partners (32 dims
-        // away) lane j ^ 4 holds.  Every lane takes part in the swap; lanes
-        // 8-15 keep the value row.
-        u32x4 y;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) y[m] = (unsigned)__shfl_xor((int)new_row[m], 4);
-        const bool second = (lane & 4) != 0;
-        const float cv[8] = {kc0[0], kc0[1], kc0[2], kc0[3], kc1[0], kc1[1], kc1[2], kc1[3]};
-        const float sv[8] = {ks0[0], ks0[1], ks0[2], ks0[3], ks1[0], ks1[1], ks1[2], ks1[3]};
-        u32x4 r;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          unsigned o[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e)
-            o[e] = bf16_rne(rope_term(bf16_lo_hi(new_row[m], e), bf16_lo_hi(y[m], e), cv[2 * m + e], sv[2 * m + e],
-                                      second));
-          r[m] = o[0] | (o[1] << 16);
-        }
-        if (lane < 8) new_row = r;
-      }
-      if (lane < 16) {
+      // With kRope the key is rotated and stored once the item's first page
+      // copies are on their way (below): the workgroup patches the new row into
+      // its own copy of the page, and no other split reads this slot.
+      if (!kRope && lane < 16) {
         const size_t dst = ((size_t)(uint32_t)page_of(k_app) * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
         *reinterpret_cast<u32x4*>((lane < 8 ? a.k_pool_w : a.v_pool_w) + dst) = new_row;
       }
@@ -367,6 +348,32 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
     }
     qb0 = __builtin_bit_cast(bf16x8, r0);
     qb1 = __builtin_bit_cast(bf16x8, r1);
+  }
+  if (kRope && k_app >= 0) {
+    // Lane j < 8 holds dims 8j..8j+7 of the new key, whose rotation partners
+    // (32 dims away) lane j ^ 4 holds.  Every lane takes part in the swap;
+    // lanes 8-15 keep the value row.
+    u32x4 y;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) y[m] = (unsigned)__shfl_xor((int)new_row[m], 4);
+    const bool second = (lane & 4) != 0;
+    const float cv[8] = {kc0[0], kc0[1], kc0[2], kc0[3], kc1[0], kc1[1], kc1[2], kc1[3]};
+    const float sv[8] = {ks0[0], ks0[1], ks0[2], ks0[3], ks1[0], ks1[1], ks1[2], ks1[3]};
+    u32x4 r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      unsigned o[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        o[e] = bf16_rne(rope_term(bf16_lo_hi(new_row[m], e), bf16_lo_hi(y[m], e), cv[2 * m + e], sv[2 * m + e],
+                                  second));
+      r[m] = o[0] | (o[1] << 16);
+    }
+    if (lane < 8) new_row = r;
+    if (lane < 16) {
+      const size_t dst = ((size_t)(uint32_t)page_of(k_app) * kPageTokens + tau_app) * kRowElems + g * kHeadDim + 8 * (lane & 7);
+      *reinterpret_cast<u32x4*>((lane < 8 ? a.k_pool_w : a.v_pool_w) + dst) = new_row;
+    }
   }
 
   for (int kb = 0; kb < n; kb += kRing) {
