@@ -21,7 +21,12 @@
  *     contiguous values (128 bytes for D = 64).
  *   - A block table per (sequence, layer): int32 [B][max_blocks] for one layer,
  *     entry j is the page of logical tokens 16j .. 16j+15.  Entries at index
- *     >= ceil(L/16) are never read (they may hold -1).
+ *     >= ceil(L/16) are never read (they may hold -1).  The entries below it
+ *     must be page ids in [0, num_pages) and L must be at most 16 * max_blocks:
+ *     pa_append, pa_decode, pa_append_decode and pa_rope_append_decode use
+ *     them as given, without a device-side check, so a value outside them
+ *     reads or writes outside the pools.  pa_fill and pa_rope_append check
+ *     both and skip the rows that fail.
  *   - seq_lens: int32 [B], the length of each sequence AFTER this step's
  *     append.  One array serves every layer of a step.
  *   - BF16 values are passed as uint16_t bit patterns.
