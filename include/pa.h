@@ -40,7 +40,8 @@
  *   - Pointers named *_pool, q, k_new, v_new, block_table, seq_lens, out,
  *     part_* and workspace are DEVICE pointers owned by the caller.  The
  *     library allocates, frees and synchronises nothing and keeps no state
- *     between calls; it is reentrant.
+ *     between calls beyond a per-device flag (atomic) that the decode
+ *     kernels' dynamic LDS limit has been raised; it is reentrant.
  *   - Arguments are validated on the host before anything is launched; on a
  *     failed check the call returns a negative status and launches nothing.
  *     B == 0 is a valid empty batch: the call returns PA_OK and launches
