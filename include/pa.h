@@ -134,7 +134,10 @@ int pa_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool, ui
  * frequency scaling.  Other sequences are skipped: their q_out rows are not
  * written and nothing is appended.
  *
- *   q, q_out      bf16 [B][Hq][D] (q_out written; it may not overlap q)
+ *   q, q_out      bf16 [B][Hq][D] (q_out written).  q_out may be q itself (the
+ *                 rotation is done in place: every row is read before it is
+ *                 written) or a buffer disjoint from it; a partial overlap is
+ *                 not allowed.
  *   k_new, v_new  bf16 [B][Hkv][D]
  *   cos_sin       fp32 [max_pos][D]
  *   k_pool, v_pool bf16 [num_pages][16][Hkv][D] (written)
@@ -238,7 +241,10 @@ int pa_prefill(const uint16_t* q, const uint16_t* k, const uint16_t* v, const in
 /*
  * Bytes of workspace pa_decode and pa_append_decode need for these sizes
  * (partition_tokens = 0: automatic split size).  Returns 0 for invalid sizes;
- * the calls report those.
+ * the calls report those.  ([README] feature list, persistent scratch buffers
+ * item: scratch is sized once up front and reused across steps, rather than
+ * allocated per call; this library never allocates, the caller owns the
+ * buffer and can keep one per stream for the whole run.)
  */
 size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_blocks,
                                  int32_t partition_tokens);
@@ -259,7 +265,11 @@ int32_t pa_default_partition_tokens(void);
  *   out          fp32 [B][Hq][D]; rows of sequences with L == 0 are set to 0
  *   scale        softmax scale (1/sqrt(D) for the model)
  *   partition_tokens  split size in tokens, a multiple of 16; values above
- *                2048 act as 2048.  A sequence of L tokens (npages = ceil(L/16)
+ *                2048 act as 2048 (a split holds at most 128 pages).  So a
+ *                value >= 16 * max_blocks gives every sequence a single pass
+ *                only while max_blocks <= 128 (the 2048-token context of the
+ *                pages' model); a longer table row still gets
+ *                ceil(L / 2048) splits.  A sequence of L tokens (npages = ceil(L/16)
  *                pages) is processed as S_b = ceil(npages / pp) splits with
  *                pp = partition_tokens / 16 pages; split s takes the pages
  *                s, s + S_b, s + 2 S_b, ...  With partition_tokens > 0 the splits
@@ -318,10 +328,15 @@ int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_p
  *
  *   part_o  fp32 [B][Hq][S][D]: split s's output, already divided by its l
  *   part_m  fp32 [B][Hq][S]: maximum over the split of x_t = scale*log2(e)*(q.K_t)
+ *           (a base-2 logit)
  *   part_l  fp32 [B][Hq][S]: sum over the split of 2^(x_t - part_m)
+ *   A state kept with natural-log maxima (m_e = max of scale*(q.K_t),
+ *   l = sum of e^(scale*(q.K_t) - m_e)) converts by part_m = m_e * log2(e);
+ *   l and o are the same in both bases, since 2^(x_t - part_m) = e^(s_t - m_e).
  *   seq_lens int32 [B] or NULL.  With seq_lens, split s of sequence b is live
- *           iff s*partition_tokens < seq_lens[b] (the splits pa_decode makes)
- *           and sequences with L == 0 get zeros; with NULL every split is live.
+ *           iff s*partition_tokens < seq_lens[b] (the splits pa_decode makes:
+ *           partition_tokens above 2048 act as 2048 here too) and sequences
+ *           with L == 0 get zeros; with NULL every split is live.
  *   A split's token set does not matter to the merge: any partition of a
  *   sequence's tokens into splits gives the same result.
  *   out     fp32 [B][Hq][D]

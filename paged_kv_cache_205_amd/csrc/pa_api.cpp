@@ -347,7 +347,8 @@ int pa_merge(const float* part_o, const float* part_m, const float* part_l,
   m.part_l = part_l;
   m.seq_lens = seq_lens;
   m.out = out;
-  m.part_tokens = seq_lens ? partition_tokens : 0;
+  // the splits pa_decode makes: partition_tokens above 2048 act as 2048 there
+  m.part_tokens = seq_lens ? (partition_tokens > kMaxPartitionTokens ? kMaxPartitionTokens : partition_tokens) : 0;
   m.S = S;
   m.skip_single = 0;
   if ((uint64_t)B * pa::kQHeads * 16 >= (1ull << 32)) return PA_ERR_SHAPE;

@@ -482,6 +482,29 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   // coherent across the XCDs' L2 caches without whole-cache write-back or
   // invalidation; each wave waits for its stores to complete before the
   // workgroup counts itself done.
+  //
+  // Ordering argument.  The counter update below is a relaxed atomic, so the
+  // HIP memory model gives no happens-before edge from these stores to the
+  // merging workgroup's loads; the order comes from how gfx950 executes
+  // agent-scope relaxed accesses, and every step of it is explicit here:
+  //  1. every partial word is stored as an agent-scope atomic (a global store
+  //     with sc1: written through the XCD's L2 to the device coherence point,
+  //     not left dirty in a non-coherent cache);
+  //  2. s_waitcnt vmcnt(0) returns only when each of this wave's stores has
+  //     been acknowledged by that point, and the barrier then makes all 8
+  //     waves' stores precede the counter update issued by thread 0;
+  //  3. the counter update is an agent-scope atomic (executed at the coherence
+  //     point, one modification order for all workgroups), so the workgroup
+  //     whose update returns nsplit - 1 is ordered after every other split's
+  //     update, hence after all of their acknowledged stores;
+  //  4. the merging workgroup issues its loads only after that return value has
+  //     come back (through LDS and a barrier), and they are agent-scope atomic
+  //     loads (sc1), which do not hit in a non-coherent L1 or L2 line and read
+  //     the coherence point.
+  // This is what an agent-scope release/acquire pair would do for data written
+  // and read only with agent-scope atomics, minus the whole-L2 write-back and
+  // invalidate that a release or acquire fence adds for plain accesses (with
+  // them in every workgroup the launch took three times as long).
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const size_t row = ((size_t)b * kQHeads + g * kGroup + r) * a.S + s;

@@ -114,6 +114,34 @@ def _stream(dev: torch.device, stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _torch_stream(dev: torch.device, stream):
+    """The launch stream as a torch stream object (the current one when None)."""
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=dev)
+
+
+def _decode_buffers(q, block_table, partition_tokens, out, workspace, stream):
+    """out and workspace for a decode call, allocated (and the workspace zero-filled)
+    on the launch stream when the caller passes none, so that the fill is ordered
+    before the kernel and the caching allocator recycles the blocks only after
+    work on that stream.  (Every binding that allocates an output does so on the
+    launch stream for the same reason.)"""
+    B, Hq, D = q.shape
+    if out is not None and workspace is not None:
+        return out, workspace
+    if q.device.type != "cuda":
+        raise ValueError("q must be a device tensor")
+    with torch.cuda.stream(_torch_stream(q.device, stream)):
+        if out is None:
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = workspace_for(B, block_table.shape[1], partition_tokens, q.device)
+    return out, workspace
+
+
 def _bf16(t, name):
     return _ptr(t, torch.bfloat16, name)
 
@@ -136,7 +164,8 @@ def pa_rope_append(q, k_new, v_new, cos_sin, k_pool, v_pool, block_table, seq_le
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
     if q_out is None:
-        q_out = torch.empty_like(q)
+        with torch.cuda.stream(_torch_stream(q.device, stream)):
+            q_out = torch.empty_like(q)
     lib = load()
     st = lib.pa_rope_append(_bf16(q, "q"), _bf16(k_new, "k_new"), _bf16(v_new, "v_new"),
                             _ptr(cos_sin, torch.float32, "cos_sin"), cos_sin.shape[0], _bf16(q_out, "q_out"),
@@ -175,7 +204,8 @@ def pa_prefill(q, k, v, cu_tokens, scale: float, out=None, weights: str = "bf16x
     if k.shape[0] != T or v.shape != k.shape:
         raise PAError("pa_prefill", -2, "q, k and v must have the same rows, k and v the same shape")
     if out is None:
-        out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
+        with torch.cuda.stream(_torch_stream(q.device, stream)):
+            out = torch.empty((T, Hq, D), dtype=torch.float32, device=q.device)
     elif tuple(out.shape) != (T, Hq, D):
         raise PAError("pa_prefill", -2, f"out must be [{T}][{Hq}][{D}]")
     lib = load()
@@ -195,7 +225,8 @@ def pa_default_partition_tokens() -> int:
 
 
 def workspace_for(B: int, max_blocks: int, partition_tokens: int = 0, device="cuda") -> Optional[torch.Tensor]:
-    """A zero-filled workspace for pa_decode / pa_append_decode (None when none is needed)."""
+    """A zero-filled workspace for pa_decode / pa_append_decode (None when none is needed),
+    allocated and filled on the current stream."""
     n = pa_decode_workspace_bytes(B, max_blocks, partition_tokens)
     return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
 
@@ -205,10 +236,7 @@ def pa_decode(q, k_pool, v_pool, block_table, seq_lens, scale: float, out=None,
     """q bf16 [B][32][64] -> out fp32 [B][32][64] (allocated if not given)."""
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = workspace_for(B, block_table.shape[1], partition_tokens, q.device)
+    out, workspace = _decode_buffers(q, block_table, partition_tokens, out, workspace, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     lib = load()
@@ -226,10 +254,7 @@ def pa_append_decode(k_new, v_new, k_pool, v_pool, q, block_table, seq_lens, sca
     """pa_append then pa_decode in one launch; returns out fp32 [B][32][64]."""
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = workspace_for(B, block_table.shape[1], partition_tokens, q.device)
+    out, workspace = _decode_buffers(q, block_table, partition_tokens, out, workspace, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     lib = load()
@@ -247,10 +272,7 @@ def pa_rope_append_decode(k_new, v_new, k_pool, v_pool, q, cos_sin, block_table,
     """RoPE of q and k_new at position L-1, the append and the decode in one launch; returns out fp32 [B][32][64]."""
     B, Hq, D = q.shape
     Hkv = k_pool.shape[2]
-    if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    if workspace is None:
-        workspace = workspace_for(B, block_table.shape[1], partition_tokens, q.device)
+    out, workspace = _decode_buffers(q, block_table, partition_tokens, out, workspace, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     lib = load()
@@ -268,7 +290,8 @@ def pa_merge(part_o, part_m, part_l, seq_lens=None, partition_tokens: int = 0, o
     """part_o fp32 [B][32][S][64], part_m / part_l fp32 [B][32][S] (base-2 maxima) -> out fp32 [B][32][64]."""
     B, Hq, S, D = part_o.shape
     if out is None:
-        out = torch.empty((B, Hq, D), dtype=torch.float32, device=part_o.device)
+        with torch.cuda.stream(_torch_stream(part_o.device, stream)):
+            out = torch.empty((B, Hq, D), dtype=torch.float32, device=part_o.device)
     lib = load()
     st = lib.pa_merge(_ptr(part_o, torch.float32, "part_o"), _ptr(part_m, torch.float32, "part_m"),
                       _ptr(part_l, torch.float32, "part_l"),

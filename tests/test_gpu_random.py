@@ -4,8 +4,15 @@ Each case draws a batch size, a table width (8 to 200 entries: the kernel reads
 whole table rows up to 128 entries and each split's own entries above) and
 lengths from 0 to the table's capacity, builds a paged state with shuffled
 pages and NaN in every unreferenced slot, and decodes it under the automatic
-split size and two fixed ones.  Sizes are kept so that the oracle finishes in
-seconds (at most ~12k attended tokens per case).
+split size and three fixed ones (16 tokens: one page per split, so the items
+outnumber the workgroups and the work queue hands most of them out).  Sizes
+are kept so that the oracle finishes in seconds: entries that are not full
+rows are scaled down to about 12k attended tokens per case, full rows (L = 16
+x table width) are kept as they are.
+
+The last test is a batch with more and longer items than the workgroups that
+take them, so that the automatic plan hands single-split items out longest
+first through the queue, compared in full.
 """
 import numpy as np
 import pytest
@@ -37,10 +44,14 @@ def draw(seed):
     cap = 16 * max_blocks
     lens = rng.integers(0, cap + 1, size=B)
     lens[rng.random(B) < 0.1] = 0
-    lens[rng.random(B) < 0.05] = cap
+    full = rng.random(B) < 0.05
+    lens[full] = cap
     budget = 12000  # attended tokens, so the oracle stays quick
-    if lens.sum() > budget:
-        lens = (lens * (budget / lens.sum())).astype(np.int64)
+    rest = int(lens[~full].sum())
+    room = max(budget - int(lens[full].sum()), budget // 4)
+    if rest > room:
+        lens[~full] = (lens[~full] * (room / rest)).astype(np.int64)
+    assert (lens[full] == cap).all()
     return max_blocks, [int(x) for x in lens]
 
 
@@ -51,7 +62,7 @@ def test_random_batch_matches_oracle(seed):
     ref = decode_ref(q, kp, vp, bt, L, 0.125)
     qd, kd, vd = dev_bf16(q), dev_bf16(kp), dev_bf16(vp)
     btd, sl = torch.from_numpy(bt).cuda(), torch.from_numpy(L).cuda()
-    for part in (0, 32, 256):
+    for part in (0, 16, 32, 256):
         say(f"random decode seed={seed} B={len(L)} max_blocks={max_blocks} tokens={int(L.sum())} partition={part}")
         out = ops.pa_decode(qd, kd, vd, btd, sl, 0.125, partition_tokens=part)
         torch.cuda.synchronize()
@@ -59,3 +70,52 @@ def test_random_batch_matches_oracle(seed):
         empty = L == 0
         assert np.all(got[empty] == 0.0), "empty sequences give zeros"
         check_close(got[~empty], ref[~empty], f"seed {seed} partition {part}")
+
+
+def queued_case(seed, B=300, max_blocks=128):
+    """A batch of B sequences of U{0..2048} tokens (some empty, some full) on
+    shuffled pages, NaN in every unreferenced slot; values drawn in one go."""
+    rng = np.random.default_rng(seed)
+    cap = 16 * max_blocks
+    lens = rng.integers(0, cap + 1, size=B)
+    lens[rng.random(B) < 0.03] = 0
+    lens[rng.random(B) < 0.05] = cap
+    lens = lens.astype(np.int32)
+    npg = (lens.astype(np.int64) + 15) // 16
+    num_pages = int(npg.sum()) + 7
+    free = rng.permutation(num_pages).astype(np.int32)
+    bt = np.full((B, max_blocks), -1, np.int32)
+    off = np.concatenate([[0], np.cumsum(npg)])
+    for b in range(B):
+        bt[b, :npg[b]] = free[off[b]:off[b + 1]]
+    kp = np.full((num_pages * 16, 8, 64), 0x7FC0, np.uint16)
+    vp = kp.copy()
+    rows = np.concatenate([bt[b, np.arange(lens[b]) // 16].astype(np.int64) * 16 + np.arange(lens[b]) % 16
+                           for b in range(B)])
+
+    def bits(shape):
+        x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32))
+        return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    kp[rows] = bits((len(rows), 8, 64))
+    vp[rows] = bits((len(rows), 8, 64))
+    q = bits((B, 32, 64))
+    return q, kp.reshape(num_pages, 16, 8, 64), vp.reshape(num_pages, 16, 8, 64), bt, lens
+
+
+def test_queued_longest_first_batch_matches_oracle():
+    """300 sequences of up to 2048 tokens: under the automatic split the plan
+    has more items (about 500) than the one-per-CU workgroups that take them,
+    averaging over 16 pages, so single-split items are handed out longest
+    first through the queue.  Every output is compared with the oracle."""
+    q, kp, vp, bt, L = queued_case(4242)
+    say(f"queued decode B={len(L)} tokens={int(L.sum())} (oracle ...)")
+    ref = decode_ref(q, kp, vp, bt, L, 0.125)
+    qd, kd, vd = dev_bf16(q), dev_bf16(kp), dev_bf16(vp)
+    btd, sl = torch.from_numpy(bt).cuda(), torch.from_numpy(L).cuda()
+    for part in (0, 16):
+        say(f"queued decode partition={part}")
+        got = ops.pa_decode(qd, kd, vd, btd, sl, 0.125, partition_tokens=part).cpu().numpy()
+        empty = L == 0
+        assert np.all(got[empty] == 0.0), "empty sequences give zeros"
+        check_close(got[~empty], ref[~empty], f"queued batch partition {part}")
