@@ -41,7 +41,10 @@
  *     part_* and workspace are DEVICE pointers owned by the caller.  The
  *     library allocates, frees and synchronises nothing and keeps no state
  *     between calls beyond a per-device flag (atomic) that the decode
- *     kernels' dynamic LDS limit has been raised; it is reentrant.
+ *     kernels' dynamic LDS limit has been raised and, for
+ *     pa_append_decode_noalloc only, its per-device scratch array and that
+ *     array's device address; it is reentrant (pa_append_decode_noalloc
+ *     calls that overlap on one GPU excepted).
  *   - Arguments are validated on the host before anything is launched; on a
  *     failed check the call returns a negative status and launches nothing.
  *     B == 0 is a valid empty batch: the call returns PA_OK and launches
@@ -76,6 +79,8 @@ extern "C" {
 #define PA_MAX_PREFILL_ROWS (1 << 30)
 #define PA_PREFILL_WEIGHTS_BF16X2 0
 #define PA_PREFILL_WEIGHTS_FP16 1
+/* Size of the device scratch array behind pa_append_decode_noalloc (64 MiB per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 enum pa_status {
   PA_OK = 0,
@@ -87,7 +92,8 @@ enum pa_status {
   PA_ERR_ALIGN = -6,       /* an array pointer is not 16-byte aligned */
   PA_ERR_REJECTED = -7,    /* pa_sched: the request's budget exceeds the whole pool */
   PA_ERR_BUDGET = -8,      /* pa_sched: growth beyond the request's reserved prefix */
-  PA_ERR_STATE = -9        /* pa_sched: the request is not active */
+  PA_ERR_STATE = -9,       /* pa_sched: the request is not active */
+  PA_ERR_SCRATCH = -10     /* pa_append_decode_noalloc: the call needs more than the fixed scratch */
 };
 
 /* Human-readable name of a status code (static string). */
@@ -320,6 +326,33 @@ int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_p
                      int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
                      int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pa_append_decode_noalloc - pa_append_decode for callers that cannot allocate
+ * device memory: code under graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It takes no workspace and allocates nothing: the split
+ * partials, counters and queue live in a device array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from the first call on that GPU until the process ends.
+ *
+ * Arguments, results and bit-identity are those of pa_append_decode.  Each call
+ * first clears the counters it uses (a kernel on `stream`, no memset), then
+ * launches the decode.  Limit: the workspace pa_decode_workspace_bytes(B, Hq,
+ * D, max_blocks, partition_tokens) would report must fit in the array, else
+ * PA_ERR_SCRATCH is returned before anything touches the device (64 MiB holds
+ * B = 64 at 128 table entries under the automatic split, B = 256 at 128
+ * entries with splits of 128 tokens or more, and any batch with
+ * partition_tokens >= 16 * max_blocks up to 2048 tokens).  Every call on a
+ * GPU shares that GPU's array and it keeps the last call's contents: calls
+ * that overlap in time on one GPU (two streams, two threads, two captured
+ * graphs replayed concurrently) race and give wrong results; issue them on one
+ * stream or order them with events.
+ */
+int pa_append_decode_noalloc(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                             uint16_t* v_pool, const uint16_t* q, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
+                             int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
+                             hipStream_t stream);
 
 /*
  * pa_merge - combine split partial states into the attention output.

@@ -2,7 +2,11 @@
 // split planning and kernel launches.  No allocation, no synchronisation.
 #include "pa.h"
 
+#include <hip/hip_runtime.h>
+
 #include <math.h>
+
+#include <atomic>
 
 #include "pa_kernels.h"
 #include "pa_prefill.h"
@@ -107,6 +111,9 @@ const char* pa_status_string(int status) {
     case PA_ERR_REJECTED: return "PA_ERR_REJECTED: the request's page budget exceeds the whole pool";
     case PA_ERR_BUDGET: return "PA_ERR_BUDGET: growth beyond the request's reserved prefix";
     case PA_ERR_STATE: return "PA_ERR_STATE: the request is not active";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: the call needs more workspace than the fixed scratch array of "
+             "pa_append_decode_noalloc holds (use pa_append_decode with a workspace)";
     default: return "unknown pa status";
   }
 }
@@ -235,7 +242,8 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
                float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages,
                int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool_w, uint16_t* v_pool_w,
-               bool fused_append, const float* cos_sin, int32_t max_pos, hipStream_t stream) {
+               bool fused_append, const float* cos_sin, int32_t max_pos, hipStream_t stream,
+               bool clear_counters = false) {
   const bool rope = cos_sin != nullptr || max_pos != 0;
   if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT ||
       num_pages <= 0 || num_pages > INT32_MAX || !isfinite(scale))
@@ -290,8 +298,36 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.queue = reinterpret_cast<int*>(ws + plan.off_q);
   a.cos_sin = cos_sin;
   a.max_pos = max_pos;
+  // the counters and the queue, which the kernel needs at zero (contiguous)
+  if (clear_counters &&
+      pa::launch_clear(a.counters, (int)((plan.off_q - plan.off_c) / sizeof(int)) + 2, stream) != hipSuccess)
+    return PA_ERR_LAUNCH;
   if (pa::launch_decode(a, grid, fused_append, rope, stream) != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode.  The workspace of pa_append_decode_noalloc is this
+// file-scope device array: every GPU the library runs on holds its own copy
+// (PA_NOALLOC_SCRATCH_BYTES) from the first use until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it only names a
+// stand-in); it passes the device address that hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept here.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of this device's scratch array, or nullptr if it cannot be found.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* found = nullptr;
+  if (hipGetSymbolAddress(&found, HIP_SYMBOL(scratch)) != hipSuccess || !found) return nullptr;
+  g_scratch_ptr[dev].store(found, std::memory_order_release);  // a racing lookup stores the same address
+  return found;
 }
 
 }  // namespace
@@ -327,6 +363,28 @@ int pa_rope_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t
   return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D,
                     num_pages, partition_tokens, workspace, workspace_bytes, k_new, v_new, k_pool,
                     v_pool, true, cos_sin, max_pos, stream);
+}
+
+int pa_append_decode_noalloc(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
+                             uint16_t* v_pool, const uint16_t* q, const int32_t* block_table,
+                             int32_t max_blocks, const int32_t* seq_lens, float scale, float* out, int32_t B,
+                             int32_t Hq, int32_t Hkv, int32_t D, int64_t num_pages, int32_t partition_tokens,
+                             hipStream_t stream) {
+  // sizes first, so that an oversized call is refused before the device is touched
+  if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT)
+    return PA_ERR_SHAPE;
+  const int dims = check_dims(Hq, Hkv, D);
+  if (dims != PA_OK) return dims;
+  Plan plan;
+  const int pst = make_plan(B > 0 ? B : 1, max_blocks, partition_tokens, &plan);
+  if (pst != PA_OK) return pst;
+  if (plan.bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  if (B == 0) return PA_OK;
+  void* ws = scratch_on_current_device();
+  if (!ws) return PA_ERR_LAUNCH;
+  return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D, num_pages,
+                    partition_tokens, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, k_new, v_new, k_pool, v_pool, true,
+                    nullptr, 0, stream, /*clear_counters=*/true);
 }
 
 int pa_merge(const float* part_o, const float* part_m, const float* part_l,

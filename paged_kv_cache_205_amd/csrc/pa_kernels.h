@@ -110,5 +110,7 @@ int auto_split_min_pages(int B);
 // rope: also rotate q and the new key by RoPE at position L-1 (needs fused_append).
 hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, bool rope, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+// Sets n ints at p to zero, with a kernel.
+hipError_t launch_clear(int* p, int n, hipStream_t stream);
 
 }  // namespace pa

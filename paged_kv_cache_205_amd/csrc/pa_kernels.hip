@@ -1069,7 +1069,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// clear: n ints set to zero (a kernel, not a memset, so that a captured graph
+// replays it like any other node).
+
+__global__ __launch_bounds__(256) void clear_kernel(int* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // launchers (host)
+
+hipError_t launch_clear(int* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int grid = std::min((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(clear_kernel, dim3(grid), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool,
                          uint16_t* v_pool, const int32_t* block_table, int max_blocks,

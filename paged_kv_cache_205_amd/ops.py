@@ -19,9 +19,10 @@ LIB_PATH = os.path.join(_PKG, "libpa.so")
 PA_OK = 0
 STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
           -4: "PA_ERR_WORKSPACE", -5: "PA_ERR_LAUNCH", -6: "PA_ERR_ALIGN", -7: "PA_ERR_REJECTED",
-          -8: "PA_ERR_BUDGET", -9: "PA_ERR_STATE"}
+          -8: "PA_ERR_BUDGET", -9: "PA_ERR_STATE", -10: "PA_ERR_SCRATCH"}
 EXPORTS = ("pa_status_string", "pa_append", "pa_rope_append", "pa_fill", "pa_prefill", "pa_decode_workspace_bytes",
-           "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_rope_append_decode", "pa_merge",
+           "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_rope_append_decode",
+           "pa_append_decode_noalloc", "pa_merge",
            "pa_sched_budget_pages", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_admit",
            "pa_sched_grow", "pa_sched_block_table", "pa_sched_finish", "pa_sched_decode_batch",
            "pa_sched_get_stats")
@@ -65,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.pa_rope_append_decode.argtypes = [P, P, P, P, P, P, I32, P, I32, P, F32, P, I32, I32, I32, I32, I64, I32, P,
                                           SZ, P]
     lib.pa_rope_append_decode.restype = ctypes.c_int
+    lib.pa_append_decode_noalloc.argtypes = [P, P, P, P, P, P, I32, P, F32, P, I32, I32, I32, I32, I64, I32, P]
+    lib.pa_append_decode_noalloc.restype = ctypes.c_int
     lib.pa_merge.argtypes = [P, P, P, P, I32, P, I32, I32, I32, I32, P]
     lib.pa_merge.restype = ctypes.c_int
     lib.pa_sched_budget_pages.argtypes = [I32, I32, I32, I32, ctypes.POINTER(I64)]
@@ -283,6 +286,23 @@ def pa_rope_append_decode(k_new, v_new, k_pool, v_pool, q, cos_sin, block_table,
                                    _ptr(out, torch.float32, "out"), B, Hq, Hkv, D, k_pool.shape[0],
                                    partition_tokens, ws_ptr, ws_n, _stream(q.device, stream))
     _check("pa_rope_append_decode", st)
+    return out
+
+
+def pa_append_decode_noalloc(k_new, v_new, k_pool, v_pool, q, block_table, seq_lens, scale: float, out,
+                             partition_tokens: int = 0, stream=None) -> torch.Tensor:
+    """pa_append_decode without a workspace (the library's fixed per-GPU scratch array).
+    out fp32 [B][32][64] must be given: this call allocates nothing."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    lib = load()
+    st = lib.pa_append_decode_noalloc(_bf16(k_new, "k_new"), _bf16(v_new, "v_new"), _bf16(k_pool, "k_pool"),
+                                      _bf16(v_pool, "v_pool"), _bf16(q, "q"),
+                                      _ptr(block_table, torch.int32, "block_table"), block_table.shape[1],
+                                      _ptr(seq_lens, torch.int32, "seq_lens"), float(scale),
+                                      _ptr(out, torch.float32, "out"), B, Hq, Hkv, D, k_pool.shape[0],
+                                      partition_tokens, _stream(q.device, stream))
+    _check("pa_append_decode_noalloc", st)
     return out
 
 
