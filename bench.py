@@ -58,6 +58,18 @@ ROPE_METRIC = ("RoPE + KV append: effective GB/s (q, new K/V and the table row r
 ROPE_BYTES_PER_SEQ = 4096 + 4096 + 2 * 1024 + 2 * 1024 + 256  # q in/out, K/V in/out, one table row
 
 
+def cpu_workers():
+    """(workers, affinity): one oracle worker per host core this process may run on,
+    capped at the CPU share the host grants one GPU job when it states one
+    (OMP_NUM_THREADS, read before the workers set it to 1)."""
+    aff = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    except ValueError:
+        share = 0
+    return max(1, min(aff, share) if share > 0 else aff), aff
+
+
 def measured_traffic(profile=None, sources=("pa_kernels.hip", "pa_kernels.h")):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it was
     taken on the current kernel source (the given csrc files); else None."""
@@ -76,6 +88,111 @@ def measured_traffic(profile=None, sources=("pa_kernels.hip", "pa_kernels.h")):
         with open(os.path.join(ROOT, "paged_kv_cache_205_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return int(m_tr.group(1)) if h.hexdigest() == m_sha.group(1) else None
+
+
+def decode_profile(sources=("pa_kernels.hip", "pa_kernels.h")):
+    """The headline decode kernel's committed rocprofv3 summary: whether it was
+    taken on the current kernel source, its calibrated HBM bytes per launch and
+    the kernel's average duration under the tracer (None where absent)."""
+    import re
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m_avg = re.search(r"kernel_avg_us: ([0-9.]+)", text)
+    return {"traffic": measured_traffic(TRAFFIC_PROFILE, sources),
+            "kernel_avg_us": float(m_avg.group(1)) if m_avg else None}
+
+
+# Workloads timed beside the headline; a step of the cache-resident ones reads
+# less than the 256 MB Infinity Cache, so each of their steps follows a 1 GiB write.
+OTHER_CONFIGS = ("tiny", "small", "fragmented", "skewed", "large")
+CACHE_RESIDENT = ("tiny", "small")
+
+
+def time_workload(name, steps, warmup, stream_gbs, flush):
+    """µs per step of one workload (one pa_append_decode per layer, automatic split),
+    its sequence-steps/s and effective KV GB/s against the spec peak and the
+    measured streaming read."""
+    import torch
+    from paged_kv_cache_205_amd import ops, synth
+    dev = "cuda"
+    lay = synth.get(name)
+    t_gen = time.perf_counter()
+    k_pool, v_pool = synth.make_pools(lay, dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
+    inputs = [synth.step_inputs(lay, l, dev) for l in range(lay.n_layers)]
+    outs = [torch.empty((lay.B, 32, 64), dtype=torch.float32, device=dev) for _ in range(lay.n_layers)]
+    ws = ops.workspace_for(lay.B, lay.max_blocks, 0, dev)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    plan = torch.empty(ops.pa_decode_plan_bytes(lay.B, lay.max_blocks, 0), dtype=torch.uint8, device=dev)
+
+    def step():
+        for l in range(lay.n_layers):
+            x = inputs[l]
+            ops.pa_append_decode(x["k_new"], x["v_new"], k_pool, v_pool, x["q"], bt[l], seq_lens, lay.scale,
+                                 out=outs[l], workspace=ws)
+
+    def step_planned():
+        ops.pa_decode_plan(seq_lens, lay.max_blocks, 0, plan=plan)
+        for l in range(lay.n_layers):
+            x = inputs[l]
+            ops.pa_decode_planned(x["q"], k_pool, v_pool, bt[l], plan, lay.scale, k_new=x["k_new"], v_new=x["v_new"],
+                                  out=outs[l], workspace=ws)
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+
+    def timed(run):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        if name in CACHE_RESIDENT:
+            times = []
+            for _ in range(steps):
+                flush.fill_(1.0)  # evicts the pool from the L2 caches and the Infinity Cache
+                e0.record()
+                run()
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            return float(np.median(times))
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_unplanned = timed(step)
+    ms_planned = timed(step_planned)
+    ms = min(ms_unplanned, ms_planned)
+    timing = ("median of the steps, each timed alone after a 1 GiB write (cold caches)" if name in CACHE_RESIDENT
+              else "back-to-back stream launches (a step reads more than the Infinity Cache holds)")
+    kv = lay.kv_bytes_per_step
+    gbs = kv / (ms * 1e-3) / 1e9
+    res = {
+        "B": lay.B,
+        "layers": lay.n_layers,
+        "kv_bytes_per_step": kv,
+        "us_per_step": round(ms * 1e3, 2),
+        "us_per_launch": round(ms * 1e3 / lay.n_layers, 3),
+        "seq_steps_per_s": round(lay.B / (ms * 1e-3), 1),
+        "kv_GBps": round(gbs, 2),
+        "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "frac_stream_read": None if stream_gbs is None else round(gbs / stream_gbs, 4),
+        "timing": timing,
+        "step": "pa_decode_plan + planned launches" if ms == ms_planned else "pa_append_decode launches",
+        "us_per_step_planned": round(ms_planned * 1e3, 2),
+        "us_per_step_unplanned": round(ms_unplanned * 1e3, 2),
+    }
+    log(f"config {name}: {res['us_per_step']} us/step, {res['kv_GBps']} GB/s (inputs built in {t_gen:.1f} s)")
+    del k_pool, v_pool, inputs, outs, ws, plan
+    torch.cuda.empty_cache()
+    return res
 
 
 def _oracle_fill(item):
@@ -123,9 +240,10 @@ def bench_fill(args, lay):
     """One step = one pa_fill per layer of every sequence's prompt rows."""
     cpu = None
     if not args.no_cpu:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        workers, aff = cpu_workers()
         log(f"cpu baseline (fill): oracle on {workers} workers ...")
         cpu = cpu_baseline_fill(lay, args.cpu_layers, workers)
+        cpu["affinity_cores"] = aff
     import torch
     from paged_kv_cache_205_amd import ops, synth
     if not torch.cuda.is_available():
@@ -248,9 +366,10 @@ def bench_rope(args, lay):
     position L - 1, the key and value appended."""
     cpu = None
     if not args.no_cpu:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        workers, aff = cpu_workers()
         log(f"cpu baseline (rope): oracle on {workers} workers ...")
         cpu = cpu_baseline_rope(lay, lay.n_layers, workers)
+        cpu["affinity_cores"] = aff
     import torch
     from paged_kv_cache_205_amd import ops, synth
     if not torch.cuda.is_available():
@@ -391,9 +510,10 @@ def bench_prefill(args, lay):
     """One step = one pa_prefill per layer over every prompt's rows."""
     cpu = None
     if not args.no_cpu:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        workers, aff = cpu_workers()
         log(f"cpu baseline (prefill): oracle on {workers} workers ...")
         cpu = cpu_baseline_prefill(lay, args.cpu_prompts, workers)
+        cpu["affinity_cores"] = aff
         log(f"cpu baseline: {cpu['value']:.6f} TFLOP/s ({cpu['seconds']} s)")
     import torch
     from paged_kv_cache_205_amd import ops, synth
@@ -599,6 +719,8 @@ def main():
     ap.add_argument("--cpu-prompts", type=int, default=192, help="prompts (layer by layer) the prefill oracle runs on")
     ap.add_argument("--prefill-weights", choices=("bf16x2", "fp16"), default="bf16x2",
                     help="prefill: weights as bf16 pairs (default) or fp16 weights with fp16 V")
+    ap.add_argument("--configs", default=",".join(OTHER_CONFIGS),
+                    help="decode: other workloads timed after the headline one (comma list, or 'none')")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -622,9 +744,10 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        workers, aff = cpu_workers()
         log(f"cpu baseline: oracle on {workers} workers ...")
         cpu = cpu_baseline(lay, args.cpu_layers, workers)
+        cpu["affinity_cores"] = aff
         log(f"cpu baseline: {cpu['value']:.4f} GB/s ({cpu['seconds']} s)")
 
     import torch
@@ -679,6 +802,27 @@ def main():
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
+
+    # the same step from a plan built once per step (pa_decode_plan, then one
+    # pa_decode_planned append + decode per layer)
+    plan = torch.empty(ops.pa_decode_plan_bytes(lay.B, lay.max_blocks, part), dtype=torch.uint8, device=dev)
+
+    def step_planned():
+        ops.pa_decode_plan(seq_lens, lay.max_blocks, part, plan=plan)
+        for l in range(lay.n_layers):
+            x = inputs[l]
+            ops.pa_decode_planned(x["q"], k_pool, v_pool, bt[l], plan, lay.scale, k_new=x["k_new"], v_new=x["v_new"],
+                                  out=outs[l], partition_tokens=part, workspace=ws)
+
+    for _ in range(args.warmup):
+        step_planned()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step_planned()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step_planned = t0.elapsed_time(t1) / args.steps
 
     # the same step as two calls per layer (pa_append, then pa_decode)
     for _ in range(args.warmup):
@@ -757,13 +901,28 @@ def main():
 
     stream_gbs = stream_read_reference(torch, dev)
 
+    # the other workloads, each on its own pool, after the headline's timings
+    configs = {}
+    names = [c for c in args.configs.split(",") if c and c != "none" and c != lay.name]
+    if names:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        for name in names:
+            configs[name] = time_workload(name, args.steps, args.warmup, stream_gbs, flush)
+        del flush
+
     kv_step = lay.kv_bytes_per_step
-    best_ms = ms_step if graph_ms is None else min(ms_step, graph_ms)
+    best_ms = min(x for x in (ms_step, graph_ms, ms_step_planned) if x is not None)
     value = kv_step / (best_ms * 1e-3) / 1e9
     # launch duration: the back-to-back stream timing divided by the launches
     # (dispatch gaps included; rocprofv3's per-kernel average is the check)
     launch_ms = ms_step / lay.n_layers
     achieved = lay.kv_bytes_per_layer / (launch_ms * 1e-3) / 1e9
+    # Counter traffic from the committed profile, attached only when it was
+    # taken on this kernel source and its traced kernel average fits inside this
+    # run's own step time (16 launches of it cannot take longer than the step).
+    prof = decode_profile() if (lay.name == "full" and args.partition == 0) else None
+    prof_avg = prof["kernel_avg_us"] if prof else None
+    prof_fits = prof_avg is not None and lay.n_layers * prof_avg <= best_ms * 1e3
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -785,13 +944,16 @@ def main():
             "layers": lay.n_layers,
             "kv_bytes_per_step": kv_step,
             "partition_tokens": part if part else "auto",
-            "timing": "graph replay" if best_ms == graph_ms else "stream launches",
+            "timing": ("graph replay" if best_ms == graph_ms else
+                       "stream launches, plan built once per step" if best_ms == ms_step_planned else
+                       "stream launches"),
             "kv_dtype": "bf16",
             "parallelism": "single GPU",
         },
         "us_per_step": round(best_ms * 1e3, 2),
         "us_per_step_stream": round(ms_step * 1e3, 2),
         "us_per_step_graph": None if graph_ms is None else round(graph_ms * 1e3, 2),
+        "us_per_step_planned": round(ms_step_planned * 1e3, 2),
         "us_per_step_each": {"median": round(float(np.median(step_ms)) * 1e3, 2),
                              "min": round(float(np.min(step_ms)) * 1e3, 2),
                              "p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2)},
@@ -808,11 +970,15 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": (measured_traffic() if (lay.name == "full" and args.partition == 0) else None),
+            "traffic": prof["traffic"] if (prof and prof_fits) else None,
             "bytes_per_launch": lay.kv_bytes_per_layer,
             "mean_launch_us": round(launch_ms * 1e3, 3),
             "event_bracketed_launch_us": round(dec_ms_mean * 1e3, 3),
+            "profile_kernel_avg_us": prof_avg,
+            "profile_frac": (None if not prof_avg else
+                             round(lay.kv_bytes_per_layer / (prof_avg * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)),
         },
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

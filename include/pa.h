@@ -328,6 +328,57 @@ int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_p
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_plan - the work plan of one decode step, built once and read by
+ * every layer's pa_decode_planned launch of that step.
+ * ([README] batched decode item: each step packs one token of every active
+ * sequence, with separate page mappings and attention lengths per sequence;
+ * the lengths are the same for all layers of the step, so the split of each
+ * sequence into work items and their assignment to workgroups are too.)
+ *
+ *   seq_lens     int32 [B] (device), the lengths after this step's append
+ *   plan         device buffer of at least pa_decode_plan_bytes(B, max_blocks,
+ *                partition_tokens) bytes, written by one small kernel on stream
+ *   partition_tokens  as for pa_decode (0: automatic); the splits are exactly
+ *                those pa_decode makes for the same lengths and value
+ * The plan holds the lengths, the split of every sequence and which workgroup
+ * runs which split (sorted by pages and dealt longest first, with no queue).
+ * It must be rebuilt whenever seq_lens changes; a plan used with lengths other
+ * than those it was built from reads the block-table entries its own lengths
+ * reach.  Returns PA_OK, PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_ALIGN,
+ * PA_ERR_WORKSPACE (plan too small) or PA_ERR_LAUNCH; B == 0 does nothing.
+ */
+size_t pa_decode_plan_bytes(int32_t B, int32_t max_blocks, int32_t partition_tokens);
+int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t partition_tokens, void* plan,
+                   size_t plan_bytes, hipStream_t stream);
+
+/*
+ * pa_decode_planned - pa_decode, pa_append_decode or pa_rope_append_decode
+ * (by which of k_new / v_new / cos_sin are given) with the work items taken
+ * from a plan of pa_decode_plan instead of being planned inside the launch.
+ * ([README] paged decode attention item, KV page pool item and feature list,
+ * as for those calls.)
+ *
+ *   k_new, v_new  NULL (attention only: the pools are read, not written), or
+ *                 both given: the append of pa_append_decode first
+ *   cos_sin, max_pos  NULL / 0, or RoPE of q and the new key as in
+ *                 pa_rope_append_decode (needs k_new, v_new; max_pos >= 16 *
+ *                 max_blocks)
+ *   plan, plan_bytes  a plan pa_decode_plan wrote for this step's lengths with
+ *                 the same B, max_blocks and partition_tokens, on a device with
+ *                 the same compute-unit count; the lengths come from it (no
+ *                 seq_lens argument)
+ *   other arguments as for pa_append_decode.
+ * out and the pools are bit-identical to the unplanned call on the same
+ * lengths.  If the plan's header does not match B, max_blocks,
+ * partition_tokens and the launch, every element of out is set to NaN.
+ */
+int pa_decode_planned(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, const float* cos_sin,
+                      int32_t max_pos, uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_table,
+                      int32_t max_blocks, float scale, float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                      int64_t num_pages, int32_t partition_tokens, const void* plan, size_t plan_bytes,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pa_append_decode_noalloc - pa_append_decode for callers that cannot allocate
  * device memory: code under graph capture, tight serving loops, harnesses that
  * forbid allocation.  It takes no workspace and allocates nothing: the split

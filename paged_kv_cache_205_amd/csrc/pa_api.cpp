@@ -95,6 +95,22 @@ int decode_grid(int32_t B, int32_t max_blocks, const Plan& p) {
   return (int)(items < cap ? items : cap);
 }
 
+// Grid of a planned decode launch: every item can have a workgroup of its own,
+// up to two workgroups per CU (the page ring leaves room for two), and no more
+// workgroups than a plan deals to.  The plan is dealt for this grid.
+int planned_grid(int32_t B, int32_t max_blocks, int32_t part_pages) {
+  const size_t items = pa::plan_max_items(B, max_blocks, part_pages);
+  size_t cap = 2 * (size_t)device_cus();
+  if (cap > (size_t)pa::kPlanMaxBins) cap = pa::kPlanMaxBins;
+  return (int)(items < cap ? items : cap);
+}
+
+// Bytes of a plan: the header and one 16-byte slot per item, plus the empty
+// slots of a last round (fewer than one grid).
+size_t plan_buffer_bytes(int32_t B, int32_t max_blocks, int32_t part_pages) {
+  return pa::kPlanHeaderBytes + (pa::plan_max_items(B, max_blocks, part_pages) + pa::kPlanMaxBins) * 16;
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,6 +248,29 @@ size_t pa_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_b
   return p.bytes;
 }
 
+size_t pa_decode_plan_bytes(int32_t B, int32_t max_blocks, int32_t partition_tokens) {
+  if (B <= 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return 0;
+  Plan p;
+  if (make_plan(B, max_blocks, partition_tokens, &p) != PA_OK) return 0;
+  return plan_buffer_bytes(B, max_blocks, p.part_pages);
+}
+
+int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32_t partition_tokens, void* plan,
+                   size_t plan_bytes, hipStream_t stream) {
+  if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT) return PA_ERR_SHAPE;
+  Plan p;
+  const int pst = make_plan(B > 0 ? B : 1, max_blocks, partition_tokens, &p);
+  if (pst != PA_OK) return pst;
+  if (B == 0) return PA_OK;
+  if (!seq_lens || !plan) return PA_ERR_NULL;
+  if (misaligned(plan)) return PA_ERR_ALIGN;
+  if (plan_bytes < plan_buffer_bytes(B, max_blocks, p.part_pages)) return PA_ERR_WORKSPACE;
+  if (pa::launch_plan(seq_lens, B, max_blocks, p.part_pages, device_cus(), planned_grid(B, max_blocks, p.part_pages),
+                      static_cast<int*>(plan), stream) != hipSuccess)
+    return PA_ERR_LAUNCH;
+  return PA_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -243,7 +282,8 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
                int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_pool_w, uint16_t* v_pool_w,
                bool fused_append, const float* cos_sin, int32_t max_pos, hipStream_t stream,
-               bool clear_counters = false) {
+               bool clear_counters = false, bool planned = false, const void* plan_buf = nullptr,
+               size_t plan_bytes = 0) {
   const bool rope = cos_sin != nullptr || max_pos != 0;
   if (B < 0 || B > pa::kMaxDecodeBatch || max_blocks <= 0 || max_blocks > PA_MAX_BLOCKS_LIMIT ||
       num_pages <= 0 || num_pages > INT32_MAX || !isfinite(scale))
@@ -254,7 +294,12 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   const int pst = make_plan(B > 0 ? B : 1, max_blocks, partition_tokens, &plan);
   if (pst != PA_OK) return pst;
   if (B == 0) return PA_OK;
-  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !out) return PA_ERR_NULL;
+  if (!q || !k_pool || !v_pool || !block_table || (!seq_lens && !planned) || !out) return PA_ERR_NULL;
+  if (planned) {  // the plan carries the lengths
+    if (!plan_buf) return PA_ERR_NULL;
+    if (misaligned(plan_buf)) return PA_ERR_ALIGN;
+    if (plan_bytes < plan_buffer_bytes(B, max_blocks, plan.part_pages)) return PA_ERR_WORKSPACE;
+  }
   if (fused_append && (!k_new || !v_new)) return PA_ERR_NULL;
   if (misaligned(q) || misaligned(k_pool) || misaligned(v_pool) || misaligned(out))
     return PA_ERR_ALIGN;
@@ -291,18 +336,21 @@ int run_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool
   a.guess_pp = plan.part_pages > 0 ? plan.part_pages : pa::auto_split_pages((long long)B * max_blocks, B);
   a.guess_ns = (max_blocks + a.guess_pp - 1) / a.guess_pp;
   a.guess_magic = a.guess_ns > 1 ? (uint32_t)(((1ull << 32) + a.guess_ns - 1) / a.guess_ns) : 0u;
-  const int grid = decode_grid(B, max_blocks, plan);
+  const int grid = planned ? planned_grid(B, max_blocks, plan.part_pages) : decode_grid(B, max_blocks, plan);
   // batches of long items run one workgroup per CU (the kernel decides from the lengths)
   a.narrow = device_cus();
   // the kernel uses the queue only when the plan has more items than the grid
   a.queue = reinterpret_cast<int*>(ws + plan.off_q);
   a.cos_sin = cos_sin;
   a.max_pos = max_pos;
+  a.plan = static_cast<const int*>(plan_buf);
   // the counters and the queue, which the kernel needs at zero (contiguous)
   if (clear_counters &&
       pa::launch_clear(a.counters, (int)((plan.off_q - plan.off_c) / sizeof(int)) + 2, stream) != hipSuccess)
     return PA_ERR_LAUNCH;
-  if (pa::launch_decode(a, grid, fused_append, rope, stream) != hipSuccess) return PA_ERR_LAUNCH;
+  const hipError_t err = planned ? pa::launch_decode_planned(a, grid, fused_append, rope, stream)
+                                 : pa::launch_decode(a, grid, fused_append, rope, stream);
+  if (err != hipSuccess) return PA_ERR_LAUNCH;
   return PA_OK;
 }
 
@@ -385,6 +433,20 @@ int pa_append_decode_noalloc(const uint16_t* k_new, const uint16_t* v_new, uint1
   return run_decode(q, k_pool, v_pool, block_table, max_blocks, seq_lens, scale, out, B, Hq, Hkv, D, num_pages,
                     partition_tokens, ws, (size_t)PA_NOALLOC_SCRATCH_BYTES, k_new, v_new, k_pool, v_pool, true,
                     nullptr, 0, stream, /*clear_counters=*/true);
+}
+
+int pa_decode_planned(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new, const float* cos_sin,
+                      int32_t max_pos, uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_table,
+                      int32_t max_blocks, float scale, float* out, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                      int64_t num_pages, int32_t partition_tokens, const void* plan, size_t plan_bytes,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const bool append = k_new != nullptr || v_new != nullptr;
+  if (cos_sin && !append) return PA_ERR_NULL;  // RoPE rotates the key it appends
+  if (cos_sin && max_pos <= 0) return PA_ERR_SHAPE;
+  return run_decode(q, k_pool, v_pool, block_table, max_blocks, nullptr, scale, out, B, Hq, Hkv, D, num_pages,
+                    partition_tokens, workspace, workspace_bytes, k_new, v_new, append ? k_pool : nullptr,
+                    append ? v_pool : nullptr, append, cos_sin, cos_sin ? max_pos : 0, stream,
+                    /*clear_counters=*/false, /*planned=*/true, plan, plan_bytes);
 }
 
 int pa_merge(const float* part_o, const float* part_m, const float* part_l,

@@ -47,7 +47,43 @@ struct DecodeArgs {
   float* part_l;  // [B][Hq][S]
   const float* cos_sin;  // fused RoPE only: [max_pos][D], 32 cosines then 32 sines per position
   int max_pos;           // rows of cos_sin (positions past it read its last row; the host requires >= 16 max_blocks)
+  const int* plan;       // planned decode only: a plan written by plan_kernel (PlanHeader, then the items)
 };
+
+// A decode plan: the work items of one batch, built once from seq_lens and read
+// by every layer's decode launch of the step.  The header takes the first 256
+// bytes; item i is int4 {sequence, split, splits of that sequence, its length}
+// at byte 256 + 16 i.  Workgroup w < active takes, in round r, item
+// r * active + w, or r * active + active - 1 - w when the round is reversed
+// (every other round, the last one reversed): the items are sorted by pages,
+// longest first, so this deals them out about longest-processing-time first
+// without a queue.  A batch in which every sequence has the same page count
+// keeps (sequence, split) order with no reversed rounds.
+struct PlanHeader {
+  int magic;       // kPlanMagic once written
+  int B;           // what the plan was built for
+  int max_blocks;
+  int part_pages;  // requested pages per split (0: automatic)
+  int n_items;
+  int active;      // workgroups that take items
+  int rounds;      // ceil(n_items / active)
+  int pp;          // pages per split chosen
+  int uniform_ns;  // > 0: one page count for every sequence, this many splits each, items in order
+  int uniform_pages;
+  int zigzag;      // 1: reversed rounds as above
+  int grid;        // the decode grid the plan was dealt for
+};
+constexpr int kPlanMagic = 0x504c414e;  // "PLAN"
+constexpr size_t kPlanHeaderBytes = 256;
+constexpr int kPlanMaxBins = 1024;  // workgroups a plan deals to; planned decode grids stay within it
+// Items a plan can hold for these sizes (an upper bound for any lengths).
+size_t plan_max_items(int B, int max_blocks, int part_pages);
+
+// Writes the plan of a batch (one workgroup).  grid: the decode grid.
+hipError_t launch_plan(const int32_t* seq_lens, int B, int max_blocks, int part_pages, int narrow, int grid,
+                       int* plan, hipStream_t stream);
+// Decode launch that takes its items from a.plan (the same kernels' item code).
+hipError_t launch_decode_planned(const DecodeArgs& a, int grid, bool fused_append, bool rope, hipStream_t stream);
 
 struct MergeArgs {
   int B;

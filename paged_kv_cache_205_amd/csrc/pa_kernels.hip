@@ -1030,6 +1030,285 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Plan once per step (pa_decode_plan) and decode from it (pa_decode_planned).
+//
+// The plan kernel is one workgroup.  It takes the lengths, chooses the pages per
+// split exactly as the in-kernel plan does (so a sequence's splits, and thus its
+// output bits, are the same under both), and writes every (sequence, split)
+// item into the slot of the workgroup that will run it:
+//   - items are ordered by their page count, longest first (a counting sort over
+//     the counts 0..128; the order among equal counts is not fixed, and the
+//     output does not depend on it: an item's arithmetic depends only on its
+//     sequence and split, and splits are merged in split order);
+//   - they are dealt in rounds of `active` workgroups: round 0 gives item k to
+//     workgroup k, every later round gives its k-th largest item to the
+//     workgroup with the k-th smallest load so far (load = pages + a fixed cost
+//     per item), which is longest-processing-time-first within rounds; workgroup
+//     w finds its round-r item in slot r * active + w (an empty slot holds
+//     sequence -1);
+//   - above kPlanLptItems items the rounds alternate direction instead.
+// A batch in which every sequence has the same page count keeps (sequence,
+// split) order, item i in slot i.
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanKeys = kMaxSplitPages + 1;  // pages of a split: 0 .. 128
+constexpr int kPlanLptItems = 8192;            // items dealt by load; above, alternating rounds
+constexpr int kPlanMaxGrid = kPlanMaxBins;  // decode grids of planned launches (2 per CU) stay below
+constexpr int kItemCostPages = 2;  // fixed cost of an item (its table row, first copies, output) in pages
+
+size_t plan_max_items(int B, int max_blocks, int part_pages) {
+  const int minp = part_pages > 0 ? part_pages : auto_min_pages(B);
+  const size_t all = (size_t)B * (size_t)((max_blocks + minp - 1) / minp);
+  if (part_pages > 0) return all;
+  // sum_b ceil(np_b / pp) < B + total / pp, and total / pp <= kTargetItemsMixed
+  // unless pp is capped at kMaxSplitPages, when it is at most ceil(B * max_blocks / 128)
+  const size_t capped = ((size_t)B * (size_t)max_blocks + kMaxSplitPages - 1) / kMaxSplitPages;
+  const size_t bound = (size_t)B + (capped > (size_t)kTargetItemsMixed ? capped : (size_t)kTargetItemsMixed);
+  return bound < all ? bound : all;
+}
+
+__device__ __forceinline__ int active_of(int total_pages, int n_items, int narrow, int grid) {
+  return narrow > 0 && narrow < grid && total_pages >= kLongItemPages * n_items ? narrow : grid;
+}
+
+__device__ __forceinline__ void store_item(int* plan, long slot, int b, int s, int ns, int L) {
+  reinterpret_cast<int4*>(reinterpret_cast<char*>(plan) + kPlanHeaderBytes)[slot] = int4{b, s, ns, L};
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens, int B,
+                                                           int max_blocks, int part_pages, int narrow, int grid,
+                                                           int* __restrict__ plan) {
+  __shared__ int s_red[4];                // total pages, largest count, kPageCap - smallest count, items
+  __shared__ int s_hist[kPlanKeys];       // items per split page count
+  __shared__ int s_off[kPlanKeys];        // first sorted position of each count, longest first
+  __shared__ int s_load[kPlanMaxBins];    // pages dealt to each workgroup so far
+  __shared__ int s_rank_bin[kPlanMaxBins];  // the workgroup with the k-th smallest load
+  __shared__ int s_pos_bin[kPlanLptItems];  // workgroup of each sorted position
+  __shared__ int s_len[kMaxDecodeBatch];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  if (t < 4) s_red[t] = 0;
+  for (int k = t; k < kPlanKeys; k += kPlanThreads) s_hist[k] = 0;
+  __syncthreads();
+  int tp = 0, tmax = 0, tminc = 0;
+  for (int b = t; b < B; b += kPlanThreads) {
+    // lengths outside [0, 16 max_blocks] break the caller's contract; clamped
+    // here so that the items never outgrow the plan buffer
+    const int L = min(max(seq_lens[b], 0), kPageTokens * max_blocks);
+    s_len[b] = L;
+    const int np = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
+    tp += np;
+    tmax = max(tmax, np);
+    tminc = max(tminc, kPageCap - np);
+  }
+  tp = wave_inclusive_scan(tp);
+  tmax = wave_max_nonneg(tmax);
+  tminc = wave_max_nonneg(tminc);
+  if (lane == 63) {
+    atomicAdd(&s_red[0], tp);
+    atomicMax(&s_red[1], tmax);
+    atomicMax(&s_red[2], tminc);
+  }
+  __syncthreads();
+  const int total = s_red[0], all_max = s_red[1];
+  const bool uniform = kPageCap - s_red[2] == all_max;
+  const int pp = part_pages > 0 ? part_pages
+                                : auto_pages_per_split(total, uniform ? kTargetItems : kTargetItemsMixed, auto_min_pages(B));
+  PlanHeader h;
+  h.magic = kPlanMagic;
+  h.B = B;
+  h.max_blocks = max_blocks;
+  h.part_pages = part_pages;
+  h.pp = pp;
+  h.grid = grid;
+  if (uniform) {
+    const int ns = all_max > 0 ? (all_max + pp - 1) / pp : 1;
+    const int n_items = B * ns;
+    const int act = active_of(total, n_items, narrow, grid);
+    const int rounds = (n_items + act - 1) / act;
+    for (int i = t; i < rounds * act; i += kPlanThreads) {
+      const int b = i / ns;
+      if (i < n_items)
+        store_item(plan, i, b, i - b * ns, ns, s_len[b]);
+      else
+        store_item(plan, i, -1, 0, 1, 0);
+    }
+    h.n_items = n_items;
+    h.active = act;
+    h.rounds = rounds;
+    h.uniform_ns = ns;
+    h.uniform_pages = all_max;
+    h.zigzag = 0;
+  } else {
+    // histogram of split page counts: a sequence of np pages in ns splits has
+    // np % ns splits of np / ns + 1 pages and the rest of np / ns (split s takes
+    // pages s, s + ns, ...); an empty sequence is one item of 0 pages
+    int ti = 0;
+    for (int b = t; b < B; b += kPlanThreads) {
+      const int L = s_len[b];
+      const int ns = nsplit_of(L, pp);
+      ti += ns;
+      if (L <= 0) {
+        atomicAdd(&s_hist[0], 1);
+      } else {
+        const int np = (L + kPageTokens - 1) / kPageTokens;
+        const int q = np / ns, r = np - q * ns;
+        if (r) atomicAdd(&s_hist[q + 1], r);
+        atomicAdd(&s_hist[q], ns - r);
+      }
+    }
+    ti = wave_inclusive_scan(ti);
+    if (lane == 63) atomicAdd(&s_red[3], ti);
+    __syncthreads();
+    const int n_items = s_red[3];
+    if (t < kPlanKeys) {  // items with more pages come first
+      int before = 0;
+      for (int k = kPlanKeys - 1; k > t; --k) before += s_hist[k];
+      s_off[t] = before;
+    }
+    const int act = active_of(total, n_items, narrow, grid);
+    const int rounds = (n_items + act - 1) / act;
+    const bool lpt = n_items <= kPlanLptItems && act <= kPlanMaxBins;
+    if (lpt) {
+      for (int w = t; w < act; w += kPlanThreads) s_load[w] = 0;
+      for (int r = 0; r < rounds; ++r) {
+        __syncthreads();  // loads of the previous round (and s_off) complete
+        if (r == 0) {
+          for (int k = t; k < act; k += kPlanThreads) s_rank_bin[k] = k;
+        } else {
+          for (int w = t; w < act; w += kPlanThreads) {
+            const int mine = s_load[w];
+            int rank = 0;
+            for (int j = 0; j < act; ++j) {
+              const int lj = s_load[j];
+              rank += (lj < mine) | ((lj == mine) & (j < w));
+            }
+            s_rank_bin[rank] = w;
+          }
+        }
+        __syncthreads();
+        const int n_r = min(act, n_items - r * act);
+        for (int k = t; k < n_r; k += kPlanThreads) {
+          const int p = r * act + k;
+          // the page count of sorted position p: s_off does not increase with the
+          // count, and p lies in [s_off[key], s_off[key - 1]), so key is the
+          // smallest count with s_off[key] <= p
+          int key = 0;
+          for (int lo = 0, hi = kPlanKeys - 1; lo <= hi;) {
+            const int mid = (lo + hi) >> 1;
+            if (s_off[mid] <= p) { key = mid; hi = mid - 1; } else { lo = mid + 1; }
+          }
+          const int w = s_rank_bin[k];
+          s_pos_bin[p] = w;
+          s_load[w] += key + kItemCostPages;
+        }
+      }
+    }
+    __syncthreads();
+    // place every item: sorted position from a cursor per page count, then its slot
+    if (t < kPlanKeys) s_hist[t] = s_off[t];  // s_hist becomes the cursors
+    __syncthreads();
+    for (int b = t; b < B; b += kPlanThreads) {
+      const int L = s_len[b];
+      const int ns = nsplit_of(L, pp);
+      const int np = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
+      for (int sp = 0; sp < ns; ++sp) {
+        const int key = L > 0 ? (np - sp + ns - 1) / ns : 0;
+        const int p = atomicAdd(&s_hist[key], 1);
+        const int r = p / act, k = p - r * act;
+        const int w = lpt ? s_pos_bin[p] : ((r & 1) ? act - 1 - k : k);
+        store_item(plan, (long)r * act + w, b, sp, ns, L);
+      }
+    }
+    // the last round's slots that got no item
+    const int last = (rounds - 1) * act, n_last = n_items - last;
+    if (n_last < act) {
+      for (int w = t; w < act; w += kPlanThreads) s_load[w] = 0;
+      __syncthreads();
+      for (int k = t; k < n_last; k += kPlanThreads)
+        s_load[lpt ? s_pos_bin[last + k] : (((rounds - 1) & 1) ? act - 1 - k : k)] = 1;
+      __syncthreads();
+      for (int w = t; w < act; w += kPlanThreads)
+        if (!s_load[w]) store_item(plan, (long)last + w, -1, 0, 1, 0);
+    }
+    h.n_items = n_items;
+    h.active = act;
+    h.rounds = rounds;
+    h.uniform_ns = 0;
+    h.uniform_pages = 0;
+    h.zigzag = 1;
+  }
+  if (t == 0) *reinterpret_cast<PlanHeader*>(plan) = h;
+}
+
+// Decode from a plan: the item code of decode_kernel, with the items read from
+// the plan's slots instead of a plan built in every workgroup, and no queue.
+// The header, this workgroup's first slot and the rows of the item it would get
+// if every sequence filled its table row (as in decode_kernel) load together;
+// each item's successor slot loads while the item runs.
+template <bool kAppend, bool kRope>
+__global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto ring = reinterpret_cast<unsigned char (*)[kRing][kSlotBytes]>(smem);
+  __shared__ int last_split;
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x;
+  const int4* slots = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(a.plan) + kPlanHeaderBytes);
+  const int hv = a.plan[min(lane, (int)(sizeof(PlanHeader) / sizeof(int)) - 1)];  // lane i: header word i
+  int4 it = slots[w];
+
+  const int ns_g = a.guess_ns;
+  const int b_raw = ns_g > 1 ? (int)__umulhi(blockIdx.x, a.guess_magic) : (int)blockIdx.x;
+  const int b_g = min(b_raw, a.B - 1);
+  ItemPrefetch pre;
+  pre.b = (a.max_blocks <= 128 && b_raw < a.B) ? b_raw : -1;
+  {
+    const int t = lane & 15, c = lane >> 4;
+    const int g = threadIdx.x >> 6;
+    const int32_t* bt = a.block_table + (size_t)b_g * a.max_blocks;
+    pre.id0 = bt[min(lane, a.max_blocks - 1)];
+    pre.id1 = bt[min(64 + lane, a.max_blocks - 1)];
+    const uint16_t* qrow = a.q + ((size_t)b_g * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
+    pre.q0 = ld16(qrow + 8 * c);
+    pre.q1 = ld16(qrow + 32 + 8 * c);
+    pre.row = u32x4{0u, 0u, 0u, 0u};
+    if (kAppend)
+      pre.row = ld16(((lane & 8) ? a.v_new : a.k_new) + ((size_t)b_g * kKvHeads + g) * kHeadDim + 8 * (lane & 7));
+  }
+  const DmaOffsets doff = dma_offsets(lane, threadIdx.x >> 6);
+  const int magic = __builtin_amdgcn_readlane(hv, 0);
+  const int pB = __builtin_amdgcn_readlane(hv, 1);
+  const int pmb = __builtin_amdgcn_readlane(hv, 2);
+  const int ppart = __builtin_amdgcn_readlane(hv, 3);
+  const int act = __builtin_amdgcn_readlane(hv, 5);
+  const int rounds = __builtin_amdgcn_readlane(hv, 6);
+  const int pgrid = __builtin_amdgcn_readlane(hv, 11);
+  if (magic != kPlanMagic || pB != a.B || pmb != a.max_blocks || ppart != a.part_pages || pgrid != (int)gridDim.x) {
+    // a plan built for other sizes: every output is NaN, so that the misuse shows
+    const size_t n = (size_t)a.B * kQHeads * kHeadDim;
+    for (size_t i = (size_t)blockIdx.x * 512 + threadIdx.x; i < n; i += (size_t)gridDim.x * 512)
+      a.out[i] = __builtin_nanf("");
+    return;
+  }
+  if (w >= act) return;
+  for (int r = 0;;) {
+    int b = __builtin_amdgcn_readfirstlane(it.x);
+    const int s = __builtin_amdgcn_readfirstlane(it.y);
+    const int nsplit = __builtin_amdgcn_readfirstlane(it.z);
+    const int L = __builtin_amdgcn_readfirstlane(it.w);
+    // the next round's slot, loaded while this item runs
+    if (r + 1 < rounds) it = slots[(size_t)(r + 1) * act + w];
+    if (b >= 0 && b < a.B && s >= 0 && s < nsplit) {
+      int n = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
+      n = (n - s + nsplit - 1) / nsplit;
+      decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, false, doff, ring, &last_split);
+    }
+    pre.b = -1;
+    if (++r >= rounds) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // merge: one thread per (sequence, query head, 4 dims).
 //   out = sum_s w_s o_s / sum_s w_s,  w_s = l_s 2^(m_s - max_s m_s)
 
@@ -1110,22 +1389,22 @@ int auto_split_min_pages(int B) { return auto_min_pages(B); }
 
 // Raises a decode kernel's dynamic LDS limit to what the largest batch needs,
 // once per device (the attribute belongs to the device the call is made on).
-static hipError_t allow_decode_lds(const void* kernel, int which) {
+static hipError_t allow_decode_lds(const void* kernel, int which, size_t bytes) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> done[3][kMaxDevices];
+  static std::atomic<int> done[6][kMaxDevices];
   int dev = 0;
   hipError_t err = hipGetDevice(&dev);
   if (err != hipSuccess) return err;
   if (dev >= 0 && dev < kMaxDevices && done[which][dev].load(std::memory_order_acquire)) return hipSuccess;
-  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)decode_dynamic_lds_bytes(kMaxDecodeBatch));
+  err = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (err == hipSuccess && dev >= 0 && dev < kMaxDevices) done[which][dev].store(1, std::memory_order_release);
   return err;
 }
 
 template <bool kAppend, bool kRope>
 static hipError_t launch_decode_variant(const DecodeArgs& a, int grid, int which, hipStream_t stream) {
-  const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<kAppend, kRope>), which);
+  const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_kernel<kAppend, kRope>), which,
+                                           decode_dynamic_lds_bytes(kMaxDecodeBatch));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((decode_kernel<kAppend, kRope>), dim3(grid), dim3(64 * kKvHeads), decode_dynamic_lds_bytes(a.B),
                      stream, a);
@@ -1137,6 +1416,32 @@ hipError_t launch_decode(const DecodeArgs& a, int grid, bool fused_append, bool 
   if (rope) return launch_decode_variant<true, true>(a, grid, 2, stream);
   if (fused_append) return launch_decode_variant<true, false>(a, grid, 1, stream);
   return launch_decode_variant<false, false>(a, grid, 0, stream);
+}
+
+hipError_t launch_plan(const int32_t* seq_lens, int B, int max_blocks, int part_pages, int narrow, int grid,
+                       int* plan, hipStream_t stream) {
+  if (B <= 0 || B > kMaxDecodeBatch || grid <= 0 || grid > kPlanMaxGrid) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, B, max_blocks, part_pages, narrow,
+                     grid, plan);
+  return hipGetLastError();
+}
+
+template <bool kAppend, bool kRope>
+static hipError_t launch_planned_variant(const DecodeArgs& a, int grid, int which, hipStream_t stream) {
+  const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_planned_kernel<kAppend, kRope>), which,
+                                           (size_t)kKvHeads * kRing * kSlotBytes);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((decode_planned_kernel<kAppend, kRope>), dim3(grid), dim3(64 * kKvHeads),
+                     (size_t)kKvHeads * kRing * kSlotBytes, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_planned(const DecodeArgs& a, int grid, bool fused_append, bool rope, hipStream_t stream) {
+  if (rope && !fused_append) return hipErrorInvalidValue;
+  if (grid <= 0 || grid > kPlanMaxGrid) return hipErrorInvalidValue;
+  if (rope) return launch_planned_variant<true, true>(a, grid, 5, stream);
+  if (fused_append) return launch_planned_variant<true, false>(a, grid, 4, stream);
+  return launch_planned_variant<false, false>(a, grid, 3, stream);
 }
 
 hipError_t launch_fill(const FillArgs& a, hipStream_t stream) {

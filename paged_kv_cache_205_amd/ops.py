@@ -22,7 +22,7 @@ STATUS = {0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPO
           -8: "PA_ERR_BUDGET", -9: "PA_ERR_STATE", -10: "PA_ERR_SCRATCH"}
 EXPORTS = ("pa_status_string", "pa_append", "pa_rope_append", "pa_fill", "pa_prefill", "pa_decode_workspace_bytes",
            "pa_default_partition_tokens", "pa_decode", "pa_append_decode", "pa_rope_append_decode",
-           "pa_append_decode_noalloc", "pa_merge",
+           "pa_append_decode_noalloc", "pa_decode_plan_bytes", "pa_decode_plan", "pa_decode_planned", "pa_merge",
            "pa_sched_budget_pages", "pa_sched_create", "pa_sched_destroy", "pa_sched_submit", "pa_sched_admit",
            "pa_sched_grow", "pa_sched_block_table", "pa_sched_finish", "pa_sched_decode_batch",
            "pa_sched_get_stats")
@@ -68,6 +68,13 @@ def load() -> ctypes.CDLL:
     lib.pa_rope_append_decode.restype = ctypes.c_int
     lib.pa_append_decode_noalloc.argtypes = [P, P, P, P, P, P, I32, P, F32, P, I32, I32, I32, I32, I64, I32, P]
     lib.pa_append_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_plan_bytes.argtypes = [I32, I32, I32]
+    lib.pa_decode_plan_bytes.restype = SZ
+    lib.pa_decode_plan.argtypes = [P, I32, I32, I32, P, SZ, P]
+    lib.pa_decode_plan.restype = ctypes.c_int
+    lib.pa_decode_planned.argtypes = [P, P, P, P, I32, P, P, P, I32, F32, P, I32, I32, I32, I32, I64, I32, P, SZ, P,
+                                      SZ, P]
+    lib.pa_decode_planned.restype = ctypes.c_int
     lib.pa_merge.argtypes = [P, P, P, P, I32, P, I32, I32, I32, I32, P]
     lib.pa_merge.restype = ctypes.c_int
     lib.pa_sched_budget_pages.argtypes = [I32, I32, I32, I32, ctypes.POINTER(I64)]
@@ -286,6 +293,44 @@ def pa_rope_append_decode(k_new, v_new, k_pool, v_pool, q, cos_sin, block_table,
                                    _ptr(out, torch.float32, "out"), B, Hq, Hkv, D, k_pool.shape[0],
                                    partition_tokens, ws_ptr, ws_n, _stream(q.device, stream))
     _check("pa_rope_append_decode", st)
+    return out
+
+
+def pa_decode_plan_bytes(B: int, max_blocks: int, partition_tokens: int = 0) -> int:
+    return int(load().pa_decode_plan_bytes(B, max_blocks, partition_tokens))
+
+
+def pa_decode_plan(seq_lens, max_blocks: int, partition_tokens: int = 0, plan=None, stream=None) -> torch.Tensor:
+    """The work plan of one decode step (seq_lens int32 [B] on the device), for every
+    layer's pa_decode_planned call of that step; returns the plan buffer (uint8)."""
+    B = seq_lens.shape[0]
+    if plan is None:
+        with torch.cuda.stream(_torch_stream(seq_lens.device, stream)):
+            plan = torch.empty(max(pa_decode_plan_bytes(B, max_blocks, partition_tokens), 16), dtype=torch.uint8,
+                               device=seq_lens.device)
+    st = load().pa_decode_plan(_ptr(seq_lens, torch.int32, "seq_lens"), B, max_blocks, partition_tokens,
+                               _ptr(plan, torch.uint8, "plan"), plan.numel(), _stream(seq_lens.device, stream))
+    _check("pa_decode_plan", st)
+    return plan
+
+
+def pa_decode_planned(q, k_pool, v_pool, block_table, plan, scale: float, k_new=None, v_new=None, cos_sin=None,
+                      out=None, partition_tokens: int = 0, workspace=None, stream=None) -> torch.Tensor:
+    """Decode (with the append when k_new / v_new are given, and RoPE when cos_sin is)
+    from a plan of pa_decode_plan; returns out fp32 [B][32][64]."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    out, workspace = _decode_buffers(q, block_table, partition_tokens, out, workspace, stream)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().pa_decode_planned(_bf16(q, "q"), _bf16(k_new, "k_new"), _bf16(v_new, "v_new"),
+                                  _ptr(cos_sin, torch.float32, "cos_sin"),
+                                  cos_sin.shape[0] if cos_sin is not None else 0, _bf16(k_pool, "k_pool"),
+                                  _bf16(v_pool, "v_pool"), _ptr(block_table, torch.int32, "block_table"),
+                                  block_table.shape[1], float(scale), _ptr(out, torch.float32, "out"), B, Hq, Hkv, D,
+                                  k_pool.shape[0], partition_tokens, _ptr(plan, torch.uint8, "plan"), plan.numel(),
+                                  ws_ptr, ws_n, _stream(q.device, stream))
+    _check("pa_decode_planned", st)
     return out
 
 

@@ -1,0 +1,262 @@
+"""The plan-once decode path: pa_decode_plan + pa_decode_planned.
+
+- The plan holds every (sequence, split) item exactly once, with the split rule
+  pa.h states for pa_decode (pages per split from the batch's total pages, or
+  from partition_tokens), dealt to workgroup slots round by round; empty slots
+  only in the last round.
+- Planned calls leave out and the pools bit-identical to pa_decode,
+  pa_append_decode and pa_rope_append_decode on the same lengths (the split of
+  every sequence is the same, and so is its arithmetic), on the workloads, on
+  seeded random batches and at full size; outputs match the FP64 oracle.
+- A plan built for other sizes makes every output NaN.
+- A captured step (plan + one planned call per layer) replays bit-identically.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import decode_ref
+from paged_kv_cache_205_amd import ops, synth
+from tests.helpers import Device, check_close, oracle_sequence, say
+from tests.test_oracle import random_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.load()
+
+
+def expected_splits(lens, partition_tokens):
+    """Splits per sequence as pa.h states them for pa_decode."""
+    lens = np.asarray(lens, np.int64)
+    B = len(lens)
+    pages = (lens + 15) // 16
+    if partition_tokens > 0:
+        pp = min(partition_tokens, 2048) // 16
+    else:
+        uniform = pages.min() == pages.max()
+        n = 192 if uniform else 384
+        m = 4 if B <= 64 else 8
+        pp = min(128, max(m, -(-int(pages.sum()) // n)))
+    return np.where(lens > 0, -(-pages // pp), 1), pp
+
+
+def read_plan(plan):
+    h = plan[:48].cpu().view(torch.int32).numpy()
+    hdr = dict(zip(["magic", "B", "max_blocks", "part_pages", "n_items", "active", "rounds", "pp", "uniform_ns",
+                    "uniform_pages", "zigzag", "grid"], [int(x) for x in h]))
+    n_slots = hdr["rounds"] * hdr["active"]
+    slots = plan[256:256 + 16 * n_slots].cpu().view(torch.int32).numpy().reshape(n_slots, 4)
+    return hdr, slots
+
+
+def check_plan(plan, lens, max_blocks, partition_tokens):
+    hdr, slots = read_plan(plan)
+    ns, pp = expected_splits(lens, partition_tokens)
+    assert hdr["magic"] == 0x504C414E
+    assert hdr["B"] == len(lens) and hdr["max_blocks"] == max_blocks
+    assert hdr["pp"] == pp, (hdr["pp"], pp)
+    assert hdr["n_items"] == int(ns.sum())
+    assert 1 <= hdr["active"] <= hdr["grid"]
+    assert hdr["rounds"] == -(-hdr["n_items"] // hdr["active"])
+    live = slots[slots[:, 0] >= 0]
+    assert len(live) == hdr["n_items"]
+    got = sorted((int(b), int(s)) for b, s, _, _ in live)
+    want = sorted((b, s) for b in range(len(lens)) for s in range(int(ns[b])))
+    assert got == want, "every (sequence, split) exactly once"
+    for b, s, n, L in live:
+        assert n == ns[b] and L == lens[b]
+    empty = np.nonzero(slots[:, 0] < 0)[0]
+    assert (empty >= (hdr["rounds"] - 1) * hdr["active"]).all(), "empty slots only in the last round"
+    if hdr["uniform_ns"] == 0 and hdr["rounds"] > 1:
+        # longest first: no round holds an item longer than any item of an earlier round
+        pages = (np.asarray(lens, np.int64) + 15) // 16
+        item_pages = np.array([-(-(pages[b] - s) // n) if L > 0 else 0 for b, s, n, L in slots.tolist()
+                               if b >= 0])
+        per_round = [[] for _ in range(hdr["rounds"])]
+        for i, (b, s, n, L) in enumerate(slots.tolist()):
+            if b >= 0:
+                per_round[i // hdr["active"]].append(-(-(pages[b] - s) // n) if L > 0 else 0)
+        for r in range(1, hdr["rounds"]):
+            assert max(per_round[r]) <= min(per_round[r - 1])
+        assert len(item_pages) == hdr["n_items"]
+    return hdr
+
+
+WORKLOADS = [
+    ("tiny", synth.tiny),
+    ("small", synth.small),
+    ("fragmented", lambda: synth.fragmented(B=48, n_layers=2)),
+    ("skewed", lambda: synth.skewed(B=300, n_layers=2)),
+    ("full", lambda: synth.full(B=4, n_layers=2)),
+]
+
+
+@pytest.mark.parametrize("partition", [0, 16, 256])
+@pytest.mark.parametrize("name,make", WORKLOADS, ids=[w[0] for w in WORKLOADS])
+def test_planned_matches_unplanned(name, make, partition):
+    lay = make()
+    say(f"planned {name} B={lay.B} partition={partition}")
+    d1, d2, d3 = Device(lay), Device(lay), Device(lay)
+    refs = {b: oracle_sequence(d1, 0, b) for b in range(min(lay.B, 6))}
+    plan = ops.pa_decode_plan(d1.seq_lens, lay.max_blocks, partition)
+    torch.cuda.synchronize()
+    check_plan(plan, lay.seq_lens, lay.max_blocks, partition)
+    ws = ops.workspace_for(lay.B, lay.max_blocks, partition)
+    table = synth.rope_table(lay.max_blocks * 16, device="cuda")
+    d4 = Device(lay)
+    for l in range(lay.n_layers):
+        x = d1.inputs[l]
+        # append + decode
+        a1 = ops.pa_append_decode(x["k_new"], x["v_new"], d1.k_pool, d1.v_pool, x["q"], d1.bt[l], d1.seq_lens,
+                                  lay.scale, partition_tokens=partition)
+        p1 = ops.pa_decode_planned(x["q"], d2.k_pool, d2.v_pool, d2.bt[l], plan, lay.scale, k_new=x["k_new"],
+                                   v_new=x["v_new"], partition_tokens=partition, workspace=ws)
+        assert torch.equal(a1, p1), f"layer {l}: append + decode"
+        assert torch.equal(d1.k_pool.view(torch.int16), d2.k_pool.view(torch.int16)), f"layer {l}: K pool"
+        assert torch.equal(d1.v_pool.view(torch.int16), d2.v_pool.view(torch.int16)), f"layer {l}: V pool"
+        # attention only, on the appended pools (which it does not write)
+        a0 = ops.pa_decode(x["q"], d1.k_pool, d1.v_pool, d1.bt[l], d1.seq_lens, lay.scale, partition_tokens=partition)
+        p0 = ops.pa_decode_planned(x["q"], d2.k_pool, d2.v_pool, d2.bt[l], plan, lay.scale,
+                                   partition_tokens=partition, workspace=ws)
+        assert torch.equal(a0, p0), f"layer {l}: decode"
+        assert torch.equal(d1.k_pool.view(torch.int16), d2.k_pool.view(torch.int16)), f"layer {l}: K pool read only"
+        if l == 0:
+            got = p1.cpu().numpy()
+            for b, r in refs.items():
+                check_close(got[b], r, f"{name} sequence {b}")
+        # RoPE + append + decode on a third copy against the unplanned fused call on a fourth
+        a2 = ops.pa_rope_append_decode(x["k_new"], x["v_new"], d4.k_pool, d4.v_pool, x["q"], table, d4.bt[l],
+                                       d4.seq_lens, lay.scale, partition_tokens=partition)
+        p2 = ops.pa_decode_planned(x["q"], d3.k_pool, d3.v_pool, d3.bt[l], plan, lay.scale, k_new=x["k_new"],
+                                   v_new=x["v_new"], cos_sin=table, partition_tokens=partition, workspace=ws)
+        assert torch.equal(a2, p2), f"layer {l}: RoPE + append + decode"
+        assert torch.equal(d3.k_pool.view(torch.int16), d4.k_pool.view(torch.int16)), f"layer {l}: RoPE K pool"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_planned_random_batches(seed):
+    rng = np.random.default_rng(500 + seed)
+    max_blocks = int(rng.choice([8, 40, 128, 200]))
+    B = int(rng.integers(1, 400))
+    lens = rng.integers(0, 16 * max_blocks + 1, size=B)
+    lens[rng.random(B) < 0.1] = 0
+    lens[rng.random(B) < 0.05] = 16 * max_blocks
+    if lens.sum() > 20000:
+        small = lens < 16 * max_blocks
+        lens[small] = (lens[small] * (20000 / lens.sum())).astype(np.int64)
+    q, kp, vp, bt, L = random_case(seed, Hq=32, Hkv=8, D=64, max_blocks=max_blocks, lens=[int(x) for x in lens])
+    ref = decode_ref(q, kp, vp, bt, L, 0.125)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(kp), dev(vp)
+    btd, sl = torch.from_numpy(bt).cuda(), torch.from_numpy(L).cuda()
+    for part in (0, 16, 48):
+        say(f"planned random seed={seed} B={B} max_blocks={max_blocks} tokens={int(L.sum())} partition={part}")
+        plan = ops.pa_decode_plan(sl, max_blocks, part)
+        torch.cuda.synchronize()
+        check_plan(plan, L, max_blocks, part)
+        a = ops.pa_decode(qd, kd, vd, btd, sl, 0.125, partition_tokens=part)
+        p = ops.pa_decode_planned(qd, kd, vd, btd, plan, 0.125, partition_tokens=part)
+        assert torch.equal(a, p)
+        got = p.cpu().numpy()
+        assert np.all(got[L == 0] == 0.0)
+        check_close(got[L > 0], ref[L > 0], f"seed {seed} partition {part}")
+
+
+@pytest.mark.parametrize("name", ["fragmented", "skewed", "large", "full"])
+def test_planned_full_size(name):
+    """Every layer of the full-size workloads: planned append + decode bit-identical
+    to pa_append_decode (out and pools), sampled sequences against the oracle."""
+    lay = synth.get(name)
+    say(f"planned full size {name}: B={lay.B} pool {lay.pool_bytes / 2**30:.2f} GiB")
+    d = Device(lay)
+    layers = range(lay.n_layers) if name != "large" else (0, 15)
+    sample = [(l, b) for l in (0,) for b in sorted({0, lay.B - 1, int(np.argmax(lay.seq_lens)),
+                                                     int(np.argmin(lay.seq_lens)), lay.B // 2})]
+    pages = {lb: synth.sequence_pages(d.k_pool, d.v_pool, lay, *lb) for lb in sample}
+    k2, v2 = d.k_pool.clone(), d.v_pool.clone()
+    plan = ops.pa_decode_plan(d.seq_lens, lay.max_blocks, 0)
+    torch.cuda.synchronize()
+    hdr = check_plan(plan, lay.seq_lens, lay.max_blocks, 0)
+    say(f"  plan: {hdr['n_items']} items, {hdr['active']} workgroups, {hdr['rounds']} rounds, pp {hdr['pp']}")
+    ws1 = ops.workspace_for(lay.B, lay.max_blocks, 0)
+    ws2 = ops.workspace_for(lay.B, lay.max_blocks, 0)
+    for l in layers:
+        x = d.inputs[l]
+        p = ops.pa_decode_planned(x["q"], d.k_pool, d.v_pool, d.bt[l], plan, lay.scale, k_new=x["k_new"],
+                                  v_new=x["v_new"], workspace=ws1)
+        a = ops.pa_append_decode(x["k_new"], x["v_new"], k2, v2, x["q"], d.bt[l], d.seq_lens, lay.scale,
+                                 workspace=ws2)
+        assert torch.equal(a, p), f"layer {l}: out"
+        if l == 0:
+            got = p.cpu().numpy()
+            for (ll, b) in sample:
+                kp, vp, _ = pages[(ll, b)]
+                check_close(got[b], oracle_sequence(d, ll, b, kp, vp), f"{name} seq {b}")
+    torch.cuda.synchronize()
+    assert torch.equal(d.k_pool.view(torch.int16), k2.view(torch.int16)), "K pool"
+    assert torch.equal(d.v_pool.view(torch.int16), v2.view(torch.int16)), "V pool"
+
+
+def test_mismatched_plan_gives_nan():
+    lay = synth.fragmented(B=24, n_layers=1)
+    d = Device(lay)
+    d.append(0)  # no NaN-poisoned slot is attended: only a mismatch can give NaN
+    x = d.inputs[0]
+    big = torch.empty(ops.pa_decode_plan_bytes(lay.B, lay.max_blocks, 16), dtype=torch.uint8, device="cuda")
+    plan = ops.pa_decode_plan(d.seq_lens, lay.max_blocks, 64, plan=big)
+    # decoded with another partition than the plan's: NaN everywhere
+    out = ops.pa_decode_planned(x["q"], d.k_pool, d.v_pool, d.bt[0], plan, lay.scale, partition_tokens=32)
+    assert bool(torch.isnan(out).all())
+    # a buffer that never held a plan
+    junk = torch.zeros_like(plan)
+    out = ops.pa_decode_planned(x["q"], d.k_pool, d.v_pool, d.bt[0], junk, lay.scale, partition_tokens=64)
+    assert bool(torch.isnan(out).all())
+    # the right plan
+    out = ops.pa_decode_planned(x["q"], d.k_pool, d.v_pool, d.bt[0], plan, lay.scale, partition_tokens=64)
+    assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("name", ["skewed", "full"])
+def test_planned_step_graph_replay(name):
+    """The benchmark's step (plan, then one planned append + decode per layer),
+    captured once and replayed several times with eager work between replays:
+    every replay equals the eager step."""
+    lay = synth.skewed(B=200, n_layers=4) if name == "skewed" else synth.full(B=8, n_layers=4)
+    d = Device(lay)
+    ws = ops.workspace_for(lay.B, lay.max_blocks, 0)
+    plan = torch.empty(ops.pa_decode_plan_bytes(lay.B, lay.max_blocks, 0), dtype=torch.uint8, device="cuda")
+    outs = [torch.empty((lay.B, 32, 64), dtype=torch.float32, device="cuda") for _ in range(lay.n_layers)]
+
+    def step():
+        ops.pa_decode_plan(d.seq_lens, lay.max_blocks, 0, plan=plan)
+        for l in range(lay.n_layers):
+            x = d.inputs[l]
+            ops.pa_decode_planned(x["q"], d.k_pool, d.v_pool, d.bt[l], plan, lay.scale, k_new=x["k_new"],
+                                  v_new=x["v_new"], out=outs[l], workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(lay.n_layers):
+            assert torch.equal(outs[l], eager[l]), f"replay {rep} layer {l}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
