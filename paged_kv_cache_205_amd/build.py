@@ -17,6 +17,9 @@ HIPCC_FLAGS = [
     # place, which in AGPRs costs a copy out and back (the other kernels already
     # use the VGPR form)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # every atomic here is issued by one lane; the wave-level atomic rewrite
+    # only adds instructions (and a wait for the returned value)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
 

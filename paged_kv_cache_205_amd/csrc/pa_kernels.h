@@ -52,26 +52,27 @@ struct DecodeArgs {
 
 // A decode plan: the work items of one batch, built once from seq_lens and read
 // by every layer's decode launch of the step.  The header takes the first 256
-// bytes; item i is int4 {sequence, split, splits of that sequence, its length}
-// at byte 256 + 16 i.  Workgroup w < active takes, in round r, item
-// r * active + w, or r * active + active - 1 - w when the round is reversed
-// (every other round, the last one reversed): the items are sorted by pages,
-// longest first, so this deals them out about longest-processing-time first
-// without a queue.  A batch in which every sequence has the same page count
-// keeps (sequence, split) order with no reversed rounds.
+// bytes; slot i is int4 {sequence, split, splits of that sequence, its length}
+// at byte 256 + 16 i.  The items are sorted by pages, longest first.  In the
+// first static_rounds rounds workgroup w < active runs the item in slot
+// r * active + w (round 0 in sorted order, later rounds in alternating
+// direction); the items after those rounds are in sorted order in the
+// following slots and are claimed through the workspace's queue counter.  A
+// batch in which every sequence has the same page count keeps (sequence,
+// split) order.
 struct PlanHeader {
   int magic;       // kPlanMagic once written
   int B;           // what the plan was built for
   int max_blocks;
   int part_pages;  // requested pages per split (0: automatic)
   int n_items;
-  int active;      // workgroups that take items
-  int rounds;      // ceil(n_items / active)
-  int pp;          // pages per split chosen
-  int uniform_ns;  // > 0: one page count for every sequence, this many splits each, items in order
+  int active;         // workgroups that take items
+  int static_rounds;  // rounds dealt to fixed slots
+  int pp;             // pages per split chosen
+  int uniform_ns;     // > 0: one page count for every sequence, this many splits each, items in order
   int uniform_pages;
-  int zigzag;      // 1: reversed rounds as above
-  int grid;        // the decode grid the plan was dealt for
+  int reserved;
+  int grid;  // the decode grid the plan was dealt for
 };
 constexpr int kPlanMagic = 0x504c414e;  // "PLAN"
 constexpr size_t kPlanHeaderBytes = 256;

@@ -324,11 +324,17 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 #pragma unroll
   for (int nn = 0; nn < 4; ++nn) acc[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // The appended row arrives with the table row it was loaded beside; waiting
+  // for both here (the first copies need the table row anyway) spares the LDS
+  // patch below a wait for every copy in flight.
+  if (kAppend && !kRope) asm volatile("" ::"v"(id0), "v"(id1), "v"(new_row[0]), "v"(new_row[1]), "v"(new_row[2]),
+                                      "v"(new_row[3]));
   if (!primed) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u)
       if (u < n) issue(u, page_of(u));
   }
+
   if (kRope) {
     const u32x4 x0 = __builtin_bit_cast(u32x4, qb0), x1 = __builtin_bit_cast(u32x4, qb1);
     const float cv[8] = {qc0[0], qc0[1], qc0[2], qc0[3], qc1[0], qc1[1], qc1[2], qc1[3]};
@@ -1034,27 +1040,26 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 //
 // The plan kernel is one workgroup.  It takes the lengths, chooses the pages per
 // split exactly as the in-kernel plan does (so a sequence's splits, and thus its
-// output bits, are the same under both), and writes every (sequence, split)
-// item into the slot of the workgroup that will run it:
-//   - items are ordered by their page count, longest first (a counting sort over
-//     the counts 0..128; the order among equal counts is not fixed, and the
-//     output does not depend on it: an item's arithmetic depends only on its
-//     sequence and split, and splits are merged in split order);
-//   - they are dealt in rounds of `active` workgroups: round 0 gives item k to
-//     workgroup k, every later round gives its k-th largest item to the
-//     workgroup with the k-th smallest load so far (load = pages + a fixed cost
-//     per item), which is longest-processing-time-first within rounds; workgroup
-//     w finds its round-r item in slot r * active + w (an empty slot holds
-//     sequence -1);
-//   - above kPlanLptItems items the rounds alternate direction instead.
+// output bits, are the same under both), orders the (sequence, split) items by
+// page count, longest first (a counting sort over the counts 0..128; the order
+// among equal counts is not fixed, and the output does not depend on it: an
+// item's arithmetic depends only on its sequence and split, and splits are
+// merged in split order) when they are long (see plan_kernel; short items keep
+// the order of the in-kernel plan), and deals them to the `active` workgroups:
+//   - round 0 is fixed: workgroup w runs sorted item w (slot w);
+//   - the items after it stay in sorted order in the following slots and are
+//     claimed through the queue counter by the workgroups that finish first,
+//     which balances what no cost model sees (when each workgroup starts, how
+//     long its pages take to arrive); every workgroup copies this queued part of
+//     the list into LDS at its start, so that a claim costs one atomic.
+//   (The header's static_rounds allows more fixed rounds, in alternating
+//   direction; with them the queue took longer on every workload measured.)
 // A batch in which every sequence has the same page count keeps (sequence,
-// split) order, item i in slot i.
+// split) order.
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanKeys = kMaxSplitPages + 1;  // pages of a split: 0 .. 128
-constexpr int kPlanLptItems = 8192;            // items dealt by load; above, alternating rounds
-constexpr int kPlanMaxGrid = kPlanMaxBins;  // decode grids of planned launches (2 per CU) stay below
-constexpr int kItemCostPages = 2;  // fixed cost of an item (its table row, first copies, output) in pages
+constexpr int kPlanMaxGrid = kPlanMaxBins;     // decode grids of planned launches (2 per CU) stay below
 
 size_t plan_max_items(int B, int max_blocks, int part_pages) {
   const int minp = part_pages > 0 ? part_pages : auto_min_pages(B);
@@ -1071,6 +1076,23 @@ __device__ __forceinline__ int active_of(int total_pages, int n_items, int narro
   return narrow > 0 && narrow < grid && total_pages >= kLongItemPages * n_items ? narrow : grid;
 }
 
+// Fixed rounds of a plan: round 0 (the rest goes through the queue).
+__device__ __forceinline__ int static_rounds_of(int, int) { return 1; }
+
+// Queued items a planned decode workgroup keeps in LDS beside the page ring (two
+// workgroups still fit on a CU); claims past them read the slot from memory.
+constexpr int kPlanStageItems = 960;
+constexpr size_t kPlannedLdsBytes = (size_t)kKvHeads * kRing * kSlotBytes + (size_t)kPlanStageItems * 16;
+
+// Slot of sorted item p: in the fixed rounds, r * act + the workgroup that runs
+// it; after them, p itself.
+__device__ __forceinline__ long slot_of(int p, int act, int static_rounds) {
+  const int r = p / act;
+  if (r >= static_rounds) return p;
+  const int k = p - r * act;
+  return (long)r * act + ((r & 1) ? act - 1 - k : k);
+}
+
 __device__ __forceinline__ void store_item(int* plan, long slot, int b, int s, int ns, int L) {
   reinterpret_cast<int4*>(reinterpret_cast<char*>(plan) + kPlanHeaderBytes)[slot] = int4{b, s, ns, L};
 }
@@ -1078,12 +1100,10 @@ __device__ __forceinline__ void store_item(int* plan, long slot, int b, int s, i
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ seq_lens, int B,
                                                            int max_blocks, int part_pages, int narrow, int grid,
                                                            int* __restrict__ plan) {
-  __shared__ int s_red[4];                // total pages, largest count, kPageCap - smallest count, items
-  __shared__ int s_hist[kPlanKeys];       // items per split page count
-  __shared__ int s_off[kPlanKeys];        // first sorted position of each count, longest first
-  __shared__ int s_load[kPlanMaxBins];    // pages dealt to each workgroup so far
-  __shared__ int s_rank_bin[kPlanMaxBins];  // the workgroup with the k-th smallest load
-  __shared__ int s_pos_bin[kPlanLptItems];  // workgroup of each sorted position
+  __shared__ int s_red[4];           // total pages, largest count, kPageCap - smallest count, items
+  __shared__ int s_hist[kPlanKeys];  // items per split page count, then a cursor per count
+  __shared__ int s_wsum[4];          // per-wave totals of the count scan below
+  __shared__ int s_wm[kPlanThreads / 64], s_ws[kPlanThreads / 64];  // per-wave item totals
   __shared__ int s_len[kMaxDecodeBatch];
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -1125,132 +1145,125 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     const int ns = all_max > 0 ? (all_max + pp - 1) / pp : 1;
     const int n_items = B * ns;
     const int act = active_of(total, n_items, narrow, grid);
-    const int rounds = (n_items + act - 1) / act;
-    for (int i = t; i < rounds * act; i += kPlanThreads) {
-      const int b = i / ns;
-      if (i < n_items)
-        store_item(plan, i, b, i - b * ns, ns, s_len[b]);
-      else
-        store_item(plan, i, -1, 0, 1, 0);
+    const int srounds = static_rounds_of(n_items, act);
+    for (int p = t; p < n_items; p += kPlanThreads) {
+      const int b = p / ns;
+      store_item(plan, slot_of(p, act, srounds), b, p - b * ns, ns, s_len[b]);
     }
     h.n_items = n_items;
     h.active = act;
-    h.rounds = rounds;
+    h.static_rounds = srounds;
     h.uniform_ns = ns;
     h.uniform_pages = all_max;
-    h.zigzag = 0;
   } else {
-    // histogram of split page counts: a sequence of np pages in ns splits has
-    // np % ns splits of np / ns + 1 pages and the rest of np / ns (split s takes
-    // pages s, s + ns, ...); an empty sequence is one item of 0 pages
-    int ti = 0;
-    for (int b = t; b < B; b += kPlanThreads) {
-      const int L = s_len[b];
-      const int ns = nsplit_of(L, pp);
-      ti += ns;
-      if (L <= 0) {
-        atomicAdd(&s_hist[0], 1);
-      } else {
-        const int np = (L + kPageTokens - 1) / kPageTokens;
-        const int q = np / ns, r = np - q * ns;
-        if (r) atomicAdd(&s_hist[q + 1], r);
-        atomicAdd(&s_hist[q], ns - r);
-      }
+    // Item order.  Long items (averaging kLongItemPages or more, which run one
+    // workgroup per CU): by page count, longest first, so that no long item
+    // starts late.  Short items: every split of the multi-split sequences
+    // (sequence-major), then the single-split sequences in sequence order;
+    // sorting these would give round 0 all the largest ones, whose workgroups
+    // then finish and claim at the same moment.  Thread t counts the items of
+    // sequences [t per, t per + per).
+    const int per = (B + kPlanThreads - 1) / kPlanThreads;
+    const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+    int cm = 0, cs = 0;
+    for (int b = b0; b < b1; ++b) {
+      const int ns = nsplit_of(s_len[b], pp);
+      cm += ns > 1 ? ns : 0;
+      cs += ns > 1 ? 0 : 1;
     }
-    ti = wave_inclusive_scan(ti);
-    if (lane == 63) atomicAdd(&s_red[3], ti);
+    const int w = t >> 6;
+    const int im = wave_inclusive_scan(cm), is = wave_inclusive_scan(cs);
+    if (lane == 63) {
+      s_wm[w] = im;
+      s_ws[w] = is;
+    }
     __syncthreads();
-    const int n_items = s_red[3];
-    if (t < kPlanKeys) {  // items with more pages come first
-      int before = 0;
-      for (int k = kPlanKeys - 1; k > t; --k) before += s_hist[k];
-      s_off[t] = before;
+    int om = im - cm, os = is - cs, n_multi = 0, n_single = 0;
+    for (int v = 0; v < kPlanThreads / 64; ++v) {
+      om += v < w ? s_wm[v] : 0;
+      os += v < w ? s_ws[v] : 0;
+      n_multi += s_wm[v];
+      n_single += s_ws[v];
     }
+    const int n_items = n_multi + n_single;
     const int act = active_of(total, n_items, narrow, grid);
-    const int rounds = (n_items + act - 1) / act;
-    const bool lpt = n_items <= kPlanLptItems && act <= kPlanMaxBins;
-    if (lpt) {
-      for (int w = t; w < act; w += kPlanThreads) s_load[w] = 0;
-      for (int r = 0; r < rounds; ++r) {
-        __syncthreads();  // loads of the previous round (and s_off) complete
-        if (r == 0) {
-          for (int k = t; k < act; k += kPlanThreads) s_rank_bin[k] = k;
+    const int srounds = static_rounds_of(n_items, act);
+    if (total < kLongItemPages * n_items) {
+      for (int b = b0; b < b1; ++b) {
+        const int L = s_len[b];
+        const int ns = nsplit_of(L, pp);
+        if (ns > 1) {
+          for (int sp = 0; sp < ns; ++sp) store_item(plan, slot_of(om++, act, srounds), b, sp, ns, L);
         } else {
-          for (int w = t; w < act; w += kPlanThreads) {
-            const int mine = s_load[w];
-            int rank = 0;
-            for (int j = 0; j < act; ++j) {
-              const int lj = s_load[j];
-              rank += (lj < mine) | ((lj == mine) & (j < w));
-            }
-            s_rank_bin[rank] = w;
-          }
-        }
-        __syncthreads();
-        const int n_r = min(act, n_items - r * act);
-        for (int k = t; k < n_r; k += kPlanThreads) {
-          const int p = r * act + k;
-          // the page count of sorted position p: s_off does not increase with the
-          // count, and p lies in [s_off[key], s_off[key - 1]), so key is the
-          // smallest count with s_off[key] <= p
-          int key = 0;
-          for (int lo = 0, hi = kPlanKeys - 1; lo <= hi;) {
-            const int mid = (lo + hi) >> 1;
-            if (s_off[mid] <= p) { key = mid; hi = mid - 1; } else { lo = mid + 1; }
-          }
-          const int w = s_rank_bin[k];
-          s_pos_bin[p] = w;
-          s_load[w] += key + kItemCostPages;
+          store_item(plan, slot_of(n_multi + os++, act, srounds), b, 0, 1, L);
         }
       }
-    }
-    __syncthreads();
-    // place every item: sorted position from a cursor per page count, then its slot
-    if (t < kPlanKeys) s_hist[t] = s_off[t];  // s_hist becomes the cursors
-    __syncthreads();
-    for (int b = t; b < B; b += kPlanThreads) {
-      const int L = s_len[b];
-      const int ns = nsplit_of(L, pp);
-      const int np = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
-      for (int sp = 0; sp < ns; ++sp) {
-        const int key = L > 0 ? (np - sp + ns - 1) / ns : 0;
-        const int p = atomicAdd(&s_hist[key], 1);
-        const int r = p / act, k = p - r * act;
-        const int w = lpt ? s_pos_bin[p] : ((r & 1) ? act - 1 - k : k);
-        store_item(plan, (long)r * act + w, b, sp, ns, L);
+    } else {
+      // histogram of split page counts: a sequence of np pages in ns splits has
+      // np % ns splits of np / ns + 1 pages and the rest of np / ns (split s
+      // takes pages s, s + ns, ...); an empty sequence is one item of 0 pages
+      for (int b = b0; b < b1; ++b) {
+        const int L = s_len[b];
+        const int ns = nsplit_of(L, pp);
+        if (L <= 0) {
+          atomicAdd(&s_hist[0], 1);
+        } else {
+          const int np = (L + kPageTokens - 1) / kPageTokens;
+          const int q = np / ns, r = np - q * ns;
+          if (r) atomicAdd(&s_hist[q + 1], r);
+          atomicAdd(&s_hist[q], ns - r);
+        }
       }
-    }
-    // the last round's slots that got no item
-    const int last = (rounds - 1) * act, n_last = n_items - last;
-    if (n_last < act) {
-      for (int w = t; w < act; w += kPlanThreads) s_load[w] = 0;
       __syncthreads();
-      for (int k = t; k < n_last; k += kPlanThreads)
-        s_load[lpt ? s_pos_bin[last + k] : (((rounds - 1) & 1) ? act - 1 - k : k)] = 1;
+      // first sorted position of each count, longest first: a prefix sum over
+      // the counts taken from 128 down (three waves, 64 counts each)
+      int incl = 0, mine = 0;
+      if (w < 3) {
+        const int key = kPlanKeys - 1 - t;
+        mine = key >= 0 ? s_hist[key] : 0;
+        incl = wave_inclusive_scan(mine);
+        if (lane == 63) s_wsum[w] = incl;
+      }
       __syncthreads();
-      for (int w = t; w < act; w += kPlanThreads)
-        if (!s_load[w]) store_item(plan, (long)last + w, -1, 0, 1, 0);
+      if (w < 3) {
+        const int key = kPlanKeys - 1 - t;
+        const int before = (w >= 1 ? s_wsum[0] : 0) + (w >= 2 ? s_wsum[1] : 0);
+        if (key >= 0) s_hist[key] = before + incl - mine;  // s_hist now holds the cursors
+      }
+      __syncthreads();
+      for (int b = b0; b < b1; ++b) {
+        const int L = s_len[b];
+        const int ns = nsplit_of(L, pp);
+        const int np = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
+        for (int sp = 0; sp < ns; ++sp) {
+          const int key = L > 0 ? (np - sp + ns - 1) / ns : 0;
+          const int p = atomicAdd(&s_hist[key], 1);
+          store_item(plan, slot_of(p, act, srounds), b, sp, ns, L);
+        }
+      }
     }
     h.n_items = n_items;
     h.active = act;
-    h.rounds = rounds;
+    h.static_rounds = srounds;
     h.uniform_ns = 0;
     h.uniform_pages = 0;
-    h.zigzag = 1;
   }
   if (t == 0) *reinterpret_cast<PlanHeader*>(plan) = h;
 }
 
 // Decode from a plan: the item code of decode_kernel, with the items read from
-// the plan's slots instead of a plan built in every workgroup, and no queue.
-// The header, this workgroup's first slot and the rows of the item it would get
-// if every sequence filled its table row (as in decode_kernel) load together;
-// each item's successor slot loads while the item runs.
+// the plan's slots instead of a plan built in every workgroup.  The header, this
+// workgroup's first slot and the rows of the item it would get if every
+// sequence filled its table row (as in decode_kernel) load together; the next
+// fixed round's slot loads while an item runs; after the fixed rounds the
+// workgroup claims the remaining items through the queue counter.
 template <bool kAppend, bool kRope>
 __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   auto ring = reinterpret_cast<unsigned char (*)[kRing][kSlotBytes]>(smem);
+  unsigned char* stage = smem + (size_t)kKvHeads * kRing * kSlotBytes;  // queued slots, 16 bytes each
   __shared__ int last_split;
+  __shared__ int next_item;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x;
   const int4* slots = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(a.plan) + kPlanHeaderBytes);
@@ -1280,31 +1293,74 @@ __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
   const int pB = __builtin_amdgcn_readlane(hv, 1);
   const int pmb = __builtin_amdgcn_readlane(hv, 2);
   const int ppart = __builtin_amdgcn_readlane(hv, 3);
+  const int n_items = __builtin_amdgcn_readlane(hv, 4);
   const int act = __builtin_amdgcn_readlane(hv, 5);
-  const int rounds = __builtin_amdgcn_readlane(hv, 6);
+  const int srounds = __builtin_amdgcn_readlane(hv, 6);
   const int pgrid = __builtin_amdgcn_readlane(hv, 11);
-  if (magic != kPlanMagic || pB != a.B || pmb != a.max_blocks || ppart != a.part_pages || pgrid != (int)gridDim.x) {
+  if (magic != kPlanMagic || pB != a.B || pmb != a.max_blocks || ppart != a.part_pages || pgrid != (int)gridDim.x ||
+      act <= 0 || act > (int)gridDim.x || srounds <= 0 || n_items <= 0) {
     // a plan built for other sizes: every output is NaN, so that the misuse shows
     const size_t n = (size_t)a.B * kQHeads * kHeadDim;
     for (size_t i = (size_t)blockIdx.x * 512 + threadIdx.x; i < n; i += (size_t)gridDim.x * 512)
       a.out[i] = __builtin_nanf("");
     return;
   }
-  if (w >= act) return;
-  for (int r = 0;;) {
-    int b = __builtin_amdgcn_readfirstlane(it.x);
-    const int s = __builtin_amdgcn_readfirstlane(it.y);
-    const int nsplit = __builtin_amdgcn_readfirstlane(it.z);
-    const int L = __builtin_amdgcn_readfirstlane(it.w);
-    // the next round's slot, loaded while this item runs
-    if (r + 1 < rounds) it = slots[(size_t)(r + 1) * act + w];
-    if (b >= 0 && b < a.B && s >= 0 && s < nsplit) {
-      int n = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
-      n = (n - s + nsplit - 1) / nsplit;
-      decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, false, doff, ring, &last_split);
+  const int n_fixed = min(n_items, srounds * act);  // items in fixed slots
+  const bool queued = n_items > n_fixed;
+  const int n_stage = queued ? min(n_items - n_fixed, kPlanStageItems) : 0;
+  if (w < act && n_stage > 0) {
+    // copy the queued slots into LDS (64 per wave instruction); every wave
+    // waits for its copies before the first claim's barrier
+    const int wv = threadIdx.x >> 6;
+    for (int c = wv; c * 64 < n_stage; c += kKvHeads) {
+      const int i = min(c * 64 + lane, n_stage - 1);
+      __builtin_amdgcn_global_load_lds(slots + n_fixed + i, stage + c * 64 * 16, 16, 0, 0);
     }
-    pre.b = -1;
-    if (++r >= rounds) break;
+  }
+  if (w < act) {
+    for (int r = 0;;) {
+      const int b = __builtin_amdgcn_readfirstlane(it.x);
+      const int s = __builtin_amdgcn_readfirstlane(it.y);
+      const int nsplit = __builtin_amdgcn_readfirstlane(it.z);
+      const int L = __builtin_amdgcn_readfirstlane(it.w);
+      const bool have = r < srounds ? (long)r * act + w < n_fixed : true;
+      // the next fixed round's slot, loaded while this item runs
+      if (r + 1 < srounds && (long)(r + 1) * act + w < n_fixed) it = slots[(size_t)(r + 1) * act + w];
+      if (have && b >= 0 && b < a.B && s >= 0 && s < nsplit) {
+        int n = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
+        n = (n - s + nsplit - 1) / nsplit;
+        decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, false, doff, ring, &last_split);
+      }
+      pre.b = -1;
+      ++r;
+      if (r < srounds) {
+        if ((long)r * act + w >= n_fixed) break;
+        continue;
+      }
+      if (!queued) break;
+      // claim one of the items after the fixed rounds; the first barrier also
+      // ensures every wave has read the previous next_item and that every
+      // wave's copies of the queued slots have landed (claiming while the item
+      // still streams was slower: the workgroups of a round claim together)
+      wait_vmcnt<0>();
+      int fetched = 0;
+      if (threadIdx.x == 0)
+        fetched = n_fixed + __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (threadIdx.x == 0) next_item = fetched;
+      __syncthreads();
+      const int i = __builtin_amdgcn_readfirstlane(next_item);
+      if (i >= n_items) break;
+      it = i - n_fixed < n_stage ? *reinterpret_cast<const int4*>(stage + (size_t)(i - n_fixed) * 16) : slots[i];
+    }
+  }
+  // The last workgroup of the grid to leave resets the queue for the next call.
+  if (queued && threadIdx.x == 0) {
+    const int left = __hip_atomic_fetch_add(a.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == (int)gridDim.x - 1) {
+      __hip_atomic_store(a.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
@@ -1429,10 +1485,10 @@ hipError_t launch_plan(const int32_t* seq_lens, int B, int max_blocks, int part_
 template <bool kAppend, bool kRope>
 static hipError_t launch_planned_variant(const DecodeArgs& a, int grid, int which, hipStream_t stream) {
   const hipError_t attr = allow_decode_lds(reinterpret_cast<const void*>(decode_planned_kernel<kAppend, kRope>), which,
-                                           (size_t)kKvHeads * kRing * kSlotBytes);
+                                           kPlannedLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((decode_planned_kernel<kAppend, kRope>), dim3(grid), dim3(64 * kKvHeads),
-                     (size_t)kKvHeads * kRing * kSlotBytes, stream, a);
+  hipLaunchKernelGGL((decode_planned_kernel<kAppend, kRope>), dim3(grid), dim3(64 * kKvHeads), kPlannedLdsBytes, stream,
+                     a);
   return hipGetLastError();
 }
 

@@ -49,43 +49,52 @@ def expected_splits(lens, partition_tokens):
 
 def read_plan(plan):
     h = plan[:48].cpu().view(torch.int32).numpy()
-    hdr = dict(zip(["magic", "B", "max_blocks", "part_pages", "n_items", "active", "rounds", "pp", "uniform_ns",
-                    "uniform_pages", "zigzag", "grid"], [int(x) for x in h]))
-    n_slots = hdr["rounds"] * hdr["active"]
-    slots = plan[256:256 + 16 * n_slots].cpu().view(torch.int32).numpy().reshape(n_slots, 4)
+    hdr = dict(zip(["magic", "B", "max_blocks", "part_pages", "n_items", "active", "static_rounds", "pp",
+                    "uniform_ns", "uniform_pages", "reserved", "grid"], [int(x) for x in h]))
+    n = hdr["n_items"]
+    slots = plan[256:256 + 16 * n].cpu().view(torch.int32).numpy().reshape(n, 4)
     return hdr, slots
+
+
+def sorted_position(slot, act, static_rounds):
+    """Sorted position of the item in a slot: fixed rounds alternate direction
+    (round 0 in order), the queued items after them are in sorted order."""
+    r = slot // act
+    if r >= static_rounds:
+        return slot
+    k = slot - r * act
+    return r * act + (act - 1 - k if r % 2 else k)
 
 
 def check_plan(plan, lens, max_blocks, partition_tokens):
     hdr, slots = read_plan(plan)
     ns, pp = expected_splits(lens, partition_tokens)
+    act, sr, n = hdr["active"], hdr["static_rounds"], hdr["n_items"]
     assert hdr["magic"] == 0x504C414E
     assert hdr["B"] == len(lens) and hdr["max_blocks"] == max_blocks
     assert hdr["pp"] == pp, (hdr["pp"], pp)
-    assert hdr["n_items"] == int(ns.sum())
-    assert 1 <= hdr["active"] <= hdr["grid"]
-    assert hdr["rounds"] == -(-hdr["n_items"] // hdr["active"])
-    live = slots[slots[:, 0] >= 0]
-    assert len(live) == hdr["n_items"]
-    got = sorted((int(b), int(s)) for b, s, _, _ in live)
+    assert n == int(ns.sum())
+    assert 1 <= act <= hdr["grid"]
+    assert sr == 1, "round 0 is fixed, the rest goes through the queue"
+    got = sorted((int(b), int(s)) for b, s, _, _ in slots)
     want = sorted((b, s) for b in range(len(lens)) for s in range(int(ns[b])))
     assert got == want, "every (sequence, split) exactly once"
-    for b, s, n, L in live:
-        assert n == ns[b] and L == lens[b]
-    empty = np.nonzero(slots[:, 0] < 0)[0]
-    assert (empty >= (hdr["rounds"] - 1) * hdr["active"]).all(), "empty slots only in the last round"
-    if hdr["uniform_ns"] == 0 and hdr["rounds"] > 1:
-        # longest first: no round holds an item longer than any item of an earlier round
-        pages = (np.asarray(lens, np.int64) + 15) // 16
-        item_pages = np.array([-(-(pages[b] - s) // n) if L > 0 else 0 for b, s, n, L in slots.tolist()
-                               if b >= 0])
-        per_round = [[] for _ in range(hdr["rounds"])]
-        for i, (b, s, n, L) in enumerate(slots.tolist()):
-            if b >= 0:
-                per_round[i // hdr["active"]].append(-(-(pages[b] - s) // n) if L > 0 else 0)
-        for r in range(1, hdr["rounds"]):
-            assert max(per_round[r]) <= min(per_round[r - 1])
-        assert len(item_pages) == hdr["n_items"]
+    for b, s, nsp, L in slots:
+        assert nsp == ns[b] and L == lens[b]
+    pages = (np.asarray(lens, np.int64) + 15) // 16
+    item_pages = np.array([-(-(pages[b] - s) // nsp) if L > 0 else 0 for b, s, nsp, L in slots.tolist()])
+    order = np.empty(n, np.int64)
+    for i in range(n):
+        order[sorted_position(i, act, sr)] = i
+    assert sorted(order.tolist()) == list(range(n)), "positions are a permutation of the slots"
+    seq_order = [(b, s) for b in range(len(lens)) for s in range(int(ns[b]))]
+    if hdr["uniform_ns"] > 0:
+        assert [tuple(slots[i][:2]) for i in order] == seq_order, "one page count: (sequence, split) order"
+    elif int(pages.sum()) >= 8 * n:
+        assert (np.diff(item_pages[order]) <= 0).all(), "long items: sorted by pages, longest first"
+    else:
+        want = [(b, s) for b, s in seq_order if ns[b] > 1] + [(b, s) for b, s in seq_order if ns[b] == 1]
+        assert [tuple(slots[i][:2]) for i in order] == want, "short items: multi-split first, then sequence order"
     return hdr
 
 
@@ -184,7 +193,7 @@ def test_planned_full_size(name):
     plan = ops.pa_decode_plan(d.seq_lens, lay.max_blocks, 0)
     torch.cuda.synchronize()
     hdr = check_plan(plan, lay.seq_lens, lay.max_blocks, 0)
-    say(f"  plan: {hdr['n_items']} items, {hdr['active']} workgroups, {hdr['rounds']} rounds, pp {hdr['pp']}")
+    say(f"  plan: {hdr['n_items']} items, {hdr['active']} workgroups, {hdr['static_rounds']} fixed rounds, pp {hdr['pp']}")
     ws1 = ops.workspace_for(lay.B, lay.max_blocks, 0)
     ws2 = ops.workspace_for(lay.B, lay.max_blocks, 0)
     for l in layers:
