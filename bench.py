@@ -721,6 +721,9 @@ def main():
                     help="prefill: weights as bf16 pairs (default) or fp16 weights with fp16 V")
     ap.add_argument("--configs", default=",".join(OTHER_CONFIGS),
                     help="decode: other workloads timed after the headline one (comma list, or 'none')")
+    ap.add_argument("--pv-valu", action="store_true",
+                    help="decode: time libpa_pv_valu.so, the build whose PV product runs in FP32 on the VALU "
+                         "instead of MFMA (for the comparison; the default build uses MFMA)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -755,6 +758,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.pv_valu:
+        from paged_kv_cache_205_amd import build as _build
+        ops.LIB_PATH = _build.LIB_PV_VALU
     ops.load()
     dev = "cuda"
     log(f"workload {lay.name}: B={lay.B} layers={lay.n_layers} pool {lay.pool_bytes / 2**30:.2f} GiB, "
@@ -920,7 +926,7 @@ def main():
     # Counter traffic from the committed profile, attached only when it was
     # taken on this kernel source and its traced kernel average fits inside this
     # run's own step time (16 launches of it cannot take longer than the step).
-    prof = decode_profile() if (lay.name == "full" and args.partition == 0) else None
+    prof = decode_profile() if (lay.name == "full" and args.partition == 0 and not args.pv_valu) else None
     prof_avg = prof["kernel_avg_us"] if prof else None
     prof_fits = prof_avg is not None and lay.n_layers * prof_avg <= best_ms * 1e3
     res = {
@@ -964,7 +970,8 @@ def main():
         "stream_read_GBps": None if stream_gbs is None else round(stream_gbs, 1),
         "frac_stream_read": None if stream_gbs is None else round(value / stream_gbs, 4),
         "roofline": {
-            "kernel": "decode_kernel<fused append> (one launch per layer: append, attention, split merge)",
+            "kernel": ("decode_kernel<fused append> (one launch per layer: append, attention, split merge)"
+                       + (", PV on the VALU (comparison build)" if args.pv_valu else "")),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

@@ -31,10 +31,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP library cannot be built")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, f) for f in ("pa_api.cpp", "pa_sched.cpp", "pa_kernels.hip", "pa_prefill.hip", "pa_rope.hip")]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+# The same library with the decode's PV product on the VALU in FP32 instead of
+# MFMA (the build-time switch PA_DECODE_PV_VALU), for the measured comparison.
+LIB_PV_VALU = os.path.join(PKG, "libpa_pv_valu.so")
+SOURCES = ("pa_api.cpp", "pa_sched.cpp", "pa_kernels.hip", "pa_prefill.hip", "pa_rope.hip")
+
+
+def _build_lib(out: str, defines=(), verbose: bool = False) -> None:
+    srcs = [os.path.join(CSRC, f) for f in SOURCES]
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *defines, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            "-x", "hip", *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -44,7 +50,12 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    _build_lib(LIB, verbose=verbose)
+    _build_lib(LIB_PV_VALU, ("-DPA_DECODE_PV_VALU=1",), verbose=verbose)
     # the streaming-read reference the benchmark times beside the kernels
     probe = os.path.join(PKG, "libpa_probe.so")
     cmd = [hipcc(), *HIPCC_FLAGS, os.path.join(CSRC, "stream_probe.hip"), "-o", probe + ".tmp"]

@@ -40,6 +40,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // s_waitcnt lgkmcnt(0): all LDS (and scalar) reads of this wave have returned.
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
+// Lane I of each quad of 4 lanes, to all 4 (DPP quad_perm [I, I, I, I]).
+template <int I>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), I * 0x55, 0xf, 0xf, false));
+}
+
 __device__ __forceinline__ float lane_read(float x, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
 }
@@ -163,6 +169,11 @@ __global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
 
 #ifndef PA_RING_PAGES
 #define PA_RING_PAGES 2
+#endif
+// Build-time switch for the PV product: 0 (default) MFMA with hi/lo bf16
+// weights, 1 FP32 FMAs on the VALU (kept for the measured comparison).
+#ifndef PA_DECODE_PV_VALU
+#define PA_DECODE_PV_VALU 0
 #endif
 constexpr int kRing = PA_RING_PAGES;                     // LDS slots (pages in flight) per wave
 constexpr int kTileBytes = kPageTokens * kHeadDim * 2;   // one head's K or V rows of a page
@@ -445,6 +456,28 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
       for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_lane);
       l_lane += (p[0] + p[1]) + (p[2] + p[3]);
 
+#if PA_DECODE_PV_VALU
+      // PV on the VALU in FP32 (the measured alternative to the MFMA below):
+      // lane (t, c) adds its own 4 tokens 4c..4c+3 for all 4 heads, taking head
+      // i's weights from lane i of its quad (lane t holds head t % 4); the row
+      // groups c are summed once per split, below.
+      float pi[4][4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        pi[0][q] = quad_bcast<0>(p[q]);
+        pi[1][q] = quad_bcast<1>(p[q]);
+        pi[2][q] = quad_bcast<2>(p[q]);
+        pi[3][q] = quad_bcast<3>(p[q]);
+      }
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float v = __builtin_bit_cast(float, (unsigned)(unsigned short)vb[nn][q] << 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nn][i] = __builtin_fmaf(pi[i][q], v, acc[nn][i]);
+        }
+#else
       unsigned hi[4], lo[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -461,8 +494,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
         acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nn], acc[nn], 0, 0, 0);
         acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nn], acc[nn], 0, 0, 0);
       }
+#endif
     }
   }
+#if PA_DECODE_PV_VALU
+  // the four row groups' token sums, so that every lane holds the MFMA layout
+#pragma unroll
+  for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[nn][i] += __shfl_xor(acc[nn][i], 16);
+      acc[nn][i] += __shfl_xor(acc[nn][i], 32);
+    }
+#endif
 
   // l of head r: sum over the 4 row groups; lane r (r < 4) then holds head r.
   float lt = l_lane + __shfl_xor(l_lane, 16);
