@@ -340,11 +340,13 @@ int pa_append_decode(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_p
  *                partition_tokens) bytes, written by one small kernel on stream
  *   partition_tokens  as for pa_decode (0: automatic); the splits are exactly
  *                those pa_decode makes for the same lengths and value
- * The plan holds the lengths, the split of every sequence and which workgroup
- * runs which split (sorted by pages and dealt longest first, with no queue).
- * It must be rebuilt whenever seq_lens changes; a plan used with lengths other
- * than those it was built from reads the block-table entries its own lengths
- * reach.  Returns PA_OK, PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_ALIGN,
+ * The plan holds the lengths, the split of every sequence and the order of
+ * the (sequence, split) items: each workgroup of the decode launch takes item
+ * w first and claims the rest through the workspace's queue counter.  Long
+ * items (8 pages or more on average) are ordered by pages, longest first;
+ * shorter ones keep sequence order, multi-split sequences first.  It must be
+ * rebuilt whenever seq_lens changes; a plan used with lengths other than those
+ * it was built from reads the block-table entries its own lengths reach.  Returns PA_OK, PA_ERR_SHAPE, PA_ERR_NULL, PA_ERR_ALIGN,
  * PA_ERR_WORKSPACE (plan too small) or PA_ERR_LAUNCH; B == 0 does nothing.
  */
 size_t pa_decode_plan_bytes(int32_t B, int32_t max_blocks, int32_t partition_tokens);
@@ -367,6 +369,7 @@ int pa_decode_plan(const int32_t* seq_lens, int32_t B, int32_t max_blocks, int32
  *                 the same B, max_blocks and partition_tokens, on a device with
  *                 the same compute-unit count; the lengths come from it (no
  *                 seq_lens argument)
+ *   workspace    as for pa_decode (the same size for the same partition_tokens)
  *   other arguments as for pa_append_decode.
  * out and the pools are bit-identical to the unplanned call on the same
  * lengths.  If the plan's header does not match B, max_blocks,

@@ -53,13 +53,12 @@ struct DecodeArgs {
 // A decode plan: the work items of one batch, built once from seq_lens and read
 // by every layer's decode launch of the step.  The header takes the first 256
 // bytes; slot i is int4 {sequence, split, splits of that sequence, its length}
-// at byte 256 + 16 i.  The items are sorted by pages, longest first.  In the
-// first static_rounds rounds workgroup w < active runs the item in slot
-// r * active + w (round 0 in sorted order, later rounds in alternating
-// direction); the items after those rounds are in sorted order in the
-// following slots and are claimed through the workspace's queue counter.  A
-// batch in which every sequence has the same page count keeps (sequence,
-// split) order.
+// at byte 256 + 16 i, in the plan's order (long items by pages, longest
+// first; short ones multi-split sequences first, then sequence order; one page
+// count for all: (sequence, split) order).  In the first static_rounds rounds
+// (one, as built) workgroup w < active runs the item in slot r * active + w
+// (later fixed rounds would alternate direction); the items after them are
+// claimed in order through the workspace's queue counter.
 struct PlanHeader {
   int magic;       // kPlanMagic once written
   int B;           // what the plan was built for

@@ -1084,12 +1084,12 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
 //
 // The plan kernel is one workgroup.  It takes the lengths, chooses the pages per
 // split exactly as the in-kernel plan does (so a sequence's splits, and thus its
-// output bits, are the same under both), orders the (sequence, split) items by
-// page count, longest first (a counting sort over the counts 0..128; the order
-// among equal counts is not fixed, and the output does not depend on it: an
-// item's arithmetic depends only on its sequence and split, and splits are
-// merged in split order) when they are long (see plan_kernel; short items keep
-// the order of the in-kernel plan), and deals them to the `active` workgroups:
+// output bits, are the same under both), orders the (sequence, split) items
+// (long ones by page count, longest first, with a counting sort over the counts
+// 0..128 whose order among equal counts is not fixed; the output does not
+// depend on it: an item's arithmetic depends only on its sequence and split,
+// and splits are merged in split order; short ones as the in-kernel plan
+// orders them, see plan_kernel), and deals them to the `active` workgroups:
 //   - round 0 is fixed: workgroup w runs sorted item w (slot w);
 //   - the items after it stay in sorted order in the following slots and are
 //     claimed through the queue counter by the workgroups that finish first,
