@@ -207,6 +207,130 @@ __device__ __forceinline__ void issue_page(const DecodeArgs& a, unsigned char* d
   __builtin_amdgcn_global_load_lds(vp + o.off1, dst + kTileBytes + 1024, 16, 0, 2);
 }
 
+// One page of a split: S^T = K Q^T on MFMA, the online-softmax update of the
+// lane's head (running maximum m_lane and weight sum l_lane, base 2) and PV into
+// acc.  j: the page's index in its sequence (tokens 16 j .. 16 j + 15), L: the
+// sequence length (tokens past it are masked).
+__device__ __forceinline__ void attend_page(const u32x4& k0, const u32x4& k1, s16x4 (&vb)[4], const bf16x8& qb0,
+                                            const bf16x8& qb1, int j, int L, int c, float scale_log2,
+                                            float& m_lane, float& l_lane, f32x4 (&acc)[4]) {
+  const bool tail = (j + 1) * kPageTokens > L;
+  f32x4 st = {0.f, 0.f, 0.f, 0.f};
+  st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qb0, st, 0, 0, 0);
+  st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qb1, st, 0, 0, 0);
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (!tail || j * kPageTokens + 4 * c + r < L) ? st[r] * scale_log2 : -INFINITY;
+  if (tail) {  // masked tokens: their V slots may hold anything (NaN included)
+#pragma unroll
+    for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j * kPageTokens + 4 * c + q >= L) vb[nn][q] = 0;
+  }
+
+  const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+  if (__builtin_amdgcn_ballot_w64(xm > m_lane) != 0) {
+    // page maximum of head t%4 over the 4 row groups, then rescale
+    float pm = fmaxf(xm, __shfl_xor(xm, 16));
+    pm = fmaxf(pm, __shfl_xor(pm, 32));
+    const float mn = fmaxf(m_lane, pm);
+    const float alpha = (mn == m_lane) ? 1.f : __builtin_amdgcn_exp2f(m_lane - mn);
+    m_lane = mn;
+    l_lane *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = lane_read(alpha, r);  // lane r holds head r
+#pragma unroll
+      for (int nn = 0; nn < 4; ++nn) acc[nn][r] *= ar;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_lane);
+  l_lane += (p[0] + p[1]) + (p[2] + p[3]);
+
+#if PA_DECODE_PV_VALU
+  // PV on the VALU in FP32 (the measured alternative to the MFMA below):
+  // lane (t, c) adds its own 4 tokens 4c..4c+3 for all 4 heads, taking head
+  // i's weights from lane i of its quad (lane t holds head t % 4); the row
+  // groups c are summed once per split, in split_result.
+  float pi[4][4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    pi[0][q] = quad_bcast<0>(p[q]);
+    pi[1][q] = quad_bcast<1>(p[q]);
+    pi[2][q] = quad_bcast<2>(p[q]);
+    pi[3][q] = quad_bcast<3>(p[q]);
+  }
+#pragma unroll
+  for (int nn = 0; nn < 4; ++nn)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v = __builtin_bit_cast(float, (unsigned)(unsigned short)vb[nn][q] << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[nn][i] = __builtin_fmaf(pi[i][q], v, acc[nn][i]);
+    }
+#else
+  unsigned hi[4], lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    hi[r] = __builtin_bit_cast(unsigned, p[r]);
+    lo[r] = __builtin_bit_cast(unsigned, p[r] - __builtin_bit_cast(float, hi[r] & 0xffff0000u));
+  }
+  // pack the upper halves (bf16 truncations) of two FP32 values into one dword
+  const s16x4 ahi = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
+                                                    __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)});
+  const s16x4 alo = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
+                                                    __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)});
+#pragma unroll
+  for (int nn = 0; nn < 4; ++nn) {
+    acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nn], acc[nn], 0, 0, 0);
+    acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nn], acc[nn], 0, 0, 0);
+  }
+#endif
+}
+
+// End of a split: the per-head (l, m) and the lane's share of o.
+struct SplitResult {
+  f32x4 o;     // the lane's dims 16c + t of the 4 heads (unnormalised)
+  f32x4 l, m;  // head r's weight sum and maximum in element r (the same in every lane)
+};
+// (acc passed by value: a reference would let the selection of the lane's
+// tile below become an indexed access to memory)
+__device__ __forceinline__ SplitResult split_result(f32x4 a0, f32x4 a1, f32x4 a2, f32x4 a3, float m_lane,
+                                                    float l_lane, int c) {
+#if PA_DECODE_PV_VALU
+  // the four row groups' token sums, so that every lane holds the MFMA layout
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a0[i] += __shfl_xor(a0[i], 16);
+    a0[i] += __shfl_xor(a0[i], 32);
+    a1[i] += __shfl_xor(a1[i], 16);
+    a1[i] += __shfl_xor(a1[i], 32);
+    a2[i] += __shfl_xor(a2[i], 16);
+    a2[i] += __shfl_xor(a2[i], 32);
+    a3[i] += __shfl_xor(a3[i], 16);
+    a3[i] += __shfl_xor(a3[i], 32);
+  }
+#endif
+  SplitResult res;
+  // l of head r: sum over the 4 row groups; lane r (r < 4) then holds head r.
+  float lt = l_lane + __shfl_xor(l_lane, 16);
+  lt += __shfl_xor(lt, 32);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    res.l[r] = lane_read(lt, r);
+    res.m[r] = lane_read(m_lane, r);
+  }
+  // every row group holds the same tiles; lane (t, c) stores dim 16c + t of the 4 heads
+  res.o = a0;
+  if (c == 1) res.o = a1;
+  if (c == 2) res.o = a2;
+  if (c == 3) res.o = a3;
+  return res;
+}
+
 // Table row and q of one sequence, loaded ahead of its item (b < 0: none).
 struct ItemPrefetch {
   int b;
@@ -419,109 +543,11 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
       __builtin_amdgcn_sched_barrier(0);
       if (k + kRing < n) issue(u, page_of(k + kRing));
 
-      const int j = s + k * nsplit;  // logical page index
-      const bool tail = (j + 1) * kPageTokens > L;
-      f32x4 st = {0.f, 0.f, 0.f, 0.f};
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k0), qb0, st, 0, 0, 0);
-      st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k1), qb1, st, 0, 0, 0);
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = (!tail || j * kPageTokens + 4 * c + r < L) ? st[r] * a.scale_log2 : -INFINITY;
-      if (tail) {  // masked tokens: their V slots may hold anything (NaN included)
-#pragma unroll
-        for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (j * kPageTokens + 4 * c + q >= L) vb[nn][q] = 0;
-      }
-
-      const float xm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      if (__builtin_amdgcn_ballot_w64(xm > m_lane) != 0) {
-        // page maximum of head t%4 over the 4 row groups, then rescale
-        float pm = fmaxf(xm, __shfl_xor(xm, 16));
-        pm = fmaxf(pm, __shfl_xor(pm, 32));
-        const float mn = fmaxf(m_lane, pm);
-        const float alpha = (mn == m_lane) ? 1.f : __builtin_amdgcn_exp2f(m_lane - mn);
-        m_lane = mn;
-        l_lane *= alpha;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ar = lane_read(alpha, r);  // lane r holds head r
-#pragma unroll
-          for (int nn = 0; nn < 4; ++nn) acc[nn][r] *= ar;
-        }
-      }
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(x[r] - m_lane);
-      l_lane += (p[0] + p[1]) + (p[2] + p[3]);
-
-#if PA_DECODE_PV_VALU
-      // PV on the VALU in FP32 (the measured alternative to the MFMA below):
-      // lane (t, c) adds its own 4 tokens 4c..4c+3 for all 4 heads, taking head
-      // i's weights from lane i of its quad (lane t holds head t % 4); the row
-      // groups c are summed once per split, below.
-      float pi[4][4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        pi[0][q] = quad_bcast<0>(p[q]);
-        pi[1][q] = quad_bcast<1>(p[q]);
-        pi[2][q] = quad_bcast<2>(p[q]);
-        pi[3][q] = quad_bcast<3>(p[q]);
-      }
-#pragma unroll
-      for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = __builtin_bit_cast(float, (unsigned)(unsigned short)vb[nn][q] << 16);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[nn][i] = __builtin_fmaf(pi[i][q], v, acc[nn][i]);
-        }
-#else
-      unsigned hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hi[r] = __builtin_bit_cast(unsigned, p[r]);
-        lo[r] = __builtin_bit_cast(unsigned, p[r] - __builtin_bit_cast(float, hi[r] & 0xffff0000u));
-      }
-      // pack the upper halves (bf16 truncations) of two FP32 values into one dword
-      const s16x4 ahi = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(hi[1], hi[0], 0x07060302u),
-                                                        __builtin_amdgcn_perm(hi[3], hi[2], 0x07060302u)});
-      const s16x4 alo = __builtin_bit_cast(s16x4, u32x2{__builtin_amdgcn_perm(lo[1], lo[0], 0x07060302u),
-                                                        __builtin_amdgcn_perm(lo[3], lo[2], 0x07060302u)});
-#pragma unroll
-      for (int nn = 0; nn < 4; ++nn) {
-        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ahi, vb[nn], acc[nn], 0, 0, 0);
-        acc[nn] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(alo, vb[nn], acc[nn], 0, 0, 0);
-      }
-#endif
+      attend_page(k0, k1, vb, qb0, qb1, s + k * nsplit, L, c, a.scale_log2, m_lane, l_lane, acc);
     }
   }
-#if PA_DECODE_PV_VALU
-  // the four row groups' token sums, so that every lane holds the MFMA layout
-#pragma unroll
-  for (int nn = 0; nn < 4; ++nn)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[nn][i] += __shfl_xor(acc[nn][i], 16);
-      acc[nn][i] += __shfl_xor(acc[nn][i], 32);
-    }
-#endif
-
-  // l of head r: sum over the 4 row groups; lane r (r < 4) then holds head r.
-  float lt = l_lane + __shfl_xor(l_lane, 16);
-  lt += __shfl_xor(lt, 32);
-  float lr[4], mr[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    lr[r] = lane_read(lt, r);
-    mr[r] = lane_read(m_lane, r);
-  }
-  // every row group holds the same tiles; lane (t, c) stores dim 16c + t of the 4 heads
-  f32x4 o = acc[0];
-#pragma unroll
-  for (int nn = 1; nn < 4; ++nn)
-    if (c == nn) o = acc[nn];
+  const SplitResult sr = split_result(acc[0], acc[1], acc[2], acc[3], m_lane, l_lane, c);
+  const f32x4 o = sr.o, lr = sr.l, mr = sr.m;
   const int d = 16 * c + t;
   if (nsplit == 1) {
 #pragma unroll
