@@ -294,11 +294,12 @@ int32_t pa_default_partition_tokens(void);
  *                bytes, zero-filled before its first use.  It holds the split
  *                partials (part_o, part_m, part_l in the layout pa_merge takes,
  *                with S = ceil(max_blocks / smallest split in pages)), one int32
- *                completion counter per sequence and a work-queue counter; the
- *                counters are back at zero when the call's work completes, so
- *                the buffer can be reused without clearing.  Calls that overlap
- *                in time must not share a workspace.  Splits are combined inside
- *                the same kernel by the last workgroup of each sequence.
+ *                completion counter per (sequence, KV head) and a work-queue
+ *                counter; the counters are back at zero when the call's work
+ *                completes, so the buffer can be reused without clearing.  Calls
+ *                that overlap in time must not share a workspace.  Splits are
+ *                combined inside the same kernel, for each KV head by the last
+ *                wave of the sequence's splits to finish it.
  * Arithmetic: QK^T products of BF16 values are exact in FP32 and summed in
  * FP32; softmax and accumulation are FP32; the exponentials are base 2 with
  * log2(e) folded into the scale.

@@ -51,12 +51,12 @@ int make_plan(int32_t B, int32_t max_blocks, int32_t partition_tokens, Plan* p) 
   p->S = (max_blocks + min_pages - 1) / min_pages;
   if (p->S < 1) p->S = 1;
   // part_o [B][Hq][S][D], part_m [B][Hq][S], part_l [B][Hq][S] (only when a
-  // sequence can have several splits), counters int32 [B], queue int32 [2]
+  // sequence can have several splits), counters int32 [B][Hkv], queue int32 [2]
   const size_t rows = p->S > 1 ? (size_t)B * pa::kQHeads * p->S : 0;
   p->off_m = round_up(rows * pa::kHeadDim * sizeof(float));
   p->off_l = p->off_m + round_up(rows * sizeof(float));
   p->off_c = p->off_l + round_up(rows * sizeof(float));
-  p->off_q = p->off_c + round_up((size_t)B * sizeof(int32_t));
+  p->off_q = p->off_c + round_up((size_t)B * pa::kKvHeads * sizeof(int32_t));
   p->bytes = p->off_q + kAlign;
   return PA_OK;
 }

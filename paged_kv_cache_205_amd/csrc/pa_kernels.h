@@ -39,7 +39,7 @@ struct DecodeArgs {
   float scale_log2;  // scale * log2(e)
   uint16_t* k_pool_w;  // fused append only: the pools, writable
   uint16_t* v_pool_w;
-  int* counters;  // [B] split-completion counters, zero between calls
+  int* counters;  // [B][Hkv] split-completion counters, zero between calls
   int* queue;     // {next item, workgroups done}, zero between calls; NULL: one item per workgroup
   float* out;
   float* part_o;  // [B][Hq][S][D]

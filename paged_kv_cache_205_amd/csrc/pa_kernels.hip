@@ -164,8 +164,9 @@ __global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
 //
 // Splits.  A single-split sequence writes out directly.  Otherwise each split
 // stores its partial state (o = acc / l, m, l per query head) in the workspace,
-// and the sequence's last workgroup to finish (per-sequence atomic counter)
-// merges them: out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).
+// and for each KV head the last wave of the sequence's splits to finish (one
+// atomic counter per sequence and KV head) merges that head's 4 query heads:
+// out = sum_s w_s o_s / sum_s w_s with w_s = l_s 2^(m_s - max m).
 
 #ifndef PA_RING_PAGES
 #define PA_RING_PAGES 2
@@ -182,8 +183,6 @@ constexpr int kSlotBytes = 2 * kTileBytes;               // K tile then V tile
 // Position permutation of the 16-byte chunks inside LDS token row tau.
 __device__ __forceinline__ int swz(int tau) { return (tau & 7) ^ ((tau >> 3) << 1); }
 
-// One work item: split s (of nsplit) of sequence b, whose length is L.  Called
-// by all 8 waves of the workgroup with the same arguments.
 // DMA addressing of one page tile: instruction i loads token rows 8i..8i+7;
 // lane writes LDS bytes 16*lane of its 1 KiB, i.e. row 8i + lane/8, position
 // lane%8, which holds chunk (lane%8) ^ swz(row).
@@ -339,10 +338,13 @@ struct ItemPrefetch {
   u32x4 row;  // appended K (lanes 0-7) / V (lanes 8-15) row of the wave's head
 };
 
+// One work item: split s (of nsplit) of sequence b, whose length is L, n of its
+// pages.  Called by all 8 waves of the workgroup with the same arguments; wave
+// g handles KV head g, and the waves do not wait for one another.
 template <bool kAppend, bool kRope>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, int nsplit, int L, int n,
                                             const ItemPrefetch& pre, bool primed, DmaOffsets doff,
-                                            unsigned char (*ring)[kRing][kSlotBytes], int* last_split) {
+                                            unsigned char (*ring)[kRing][kSlotBytes]) {
   const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // lane index produced anew for every item, so that nothing derived from it is
   // hoisted out of the item loop and kept live across items
@@ -556,27 +558,27 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   }
   // Partials are written and read with device-scope (sc1) accesses, which are
   // coherent across the XCDs' L2 caches without whole-cache write-back or
-  // invalidation; each wave waits for its stores to complete before the
-  // workgroup counts itself done.
+  // invalidation.  Each wave writes the partials of its own KV head's 4 query
+  // heads and counts itself done on that (sequence, KV head)'s counter once its
+  // stores have completed; the last wave of each head merges that head, so the
+  // waves of a workgroup never wait for one another here.
   //
   // Ordering argument.  The counter update below is a relaxed atomic, so the
   // HIP memory model gives no happens-before edge from these stores to the
-  // merging workgroup's loads; the order comes from how gfx950 executes
-  // agent-scope relaxed accesses, and every step of it is explicit here:
+  // merging wave's loads; the order comes from how gfx950 executes agent-scope
+  // relaxed accesses, and every step of it is explicit here:
   //  1. every partial word is stored as an agent-scope atomic (a global store
   //     with sc1: written through the XCD's L2 to the device coherence point,
   //     not left dirty in a non-coherent cache);
   //  2. s_waitcnt vmcnt(0) returns only when each of this wave's stores has
-  //     been acknowledged by that point, and the barrier then makes all 8
-  //     waves' stores precede the counter update issued by thread 0;
+  //     been acknowledged by that point, before the wave's counter update;
   //  3. the counter update is an agent-scope atomic (executed at the coherence
-  //     point, one modification order for all workgroups), so the workgroup
-  //     whose update returns nsplit - 1 is ordered after every other split's
-  //     update, hence after all of their acknowledged stores;
-  //  4. the merging workgroup issues its loads only after that return value has
-  //     come back (through LDS and a barrier), and they are agent-scope atomic
-  //     loads (sc1), which do not hit in a non-coherent L1 or L2 line and read
-  //     the coherence point.
+  //     point, one modification order for all waves), so the wave whose update
+  //     returns nsplit - 1 is ordered after every other split's update for the
+  //     same head, hence after all of their acknowledged stores;
+  //  4. the merging wave issues its loads only after that return value has
+  //     come back, and they are agent-scope atomic loads (sc1), which do not
+  //     hit in a non-coherent L1 or L2 line and read the coherence point.
   // This is what an agent-scope release/acquire pair would do for data written
   // and read only with agent-scope atomics, minus the whole-L2 write-back and
   // invalidate that a release or acquire fence adds for plain accesses (with
@@ -592,14 +594,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   }
   wait_vmcnt<0>();
 
-  // The last workgroup of this sequence to finish combines its nsplit partial
-  // states (in split order, so the result does not depend on which one it is)
-  // and resets the sequence's counter for the next call.
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *last_split = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsplit - 1;
-  __syncthreads();
-  if (!*last_split) return;
+  // The last wave of this (sequence, KV head) to finish combines the head's
+  // nsplit partial states (in split order, so the result does not depend on
+  // which wave it is) and resets the counter for the next call.
+  int prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(a.counters + (size_t)b * kKvHeads + g, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (__builtin_amdgcn_readfirstlane(prev) != nsplit - 1) return;
   {
     const int h = lane >> 4;         // query head 4g + h
     const int d0 = (lane & 15) * 4;  // dims d0..d0+3
@@ -644,7 +645,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
     }
     *reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup + h) * kHeadDim + d0) = num * (1.f / den);
   }
-  if (threadIdx.x == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (lane == 0) __hip_atomic_store(a.counters + (size_t)b * kKvHeads + g, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 
@@ -950,7 +951,6 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   auto ring = reinterpret_cast<unsigned char (*)[kRing][kSlotBytes]>(smem);
   int* plan_arrays = reinterpret_cast<int*>(smem + kKvHeads * kRing * kSlotBytes);
   __shared__ PlanLds plan_lds;
-  __shared__ int last_split;
   __shared__ int next_item;
   const int B = a.B;
   int* sL = plan_arrays;  // [B] lengths
@@ -1057,7 +1057,7 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
   // work.  Nothing of the plan is kept in registers across an item: the next
   // item is derived from the plan in LDS.
   while (b >= 0) {
-    if (s < nsplit) decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, primed, doff, ring, &last_split);
+    if (s < nsplit) decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, primed, doff, ring);
     pre.b = -1;
     primed = false;
     b = -1;
@@ -1332,7 +1332,6 @@ __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   auto ring = reinterpret_cast<unsigned char (*)[kRing][kSlotBytes]>(smem);
   unsigned char* stage = smem + (size_t)kKvHeads * kRing * kSlotBytes;  // queued slots, 16 bytes each
-  __shared__ int last_split;
   __shared__ int next_item;
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x;
@@ -1399,7 +1398,7 @@ __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
       if (have && b >= 0 && b < a.B && s >= 0 && s < nsplit) {
         int n = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
         n = (n - s + nsplit - 1) / nsplit;
-        decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, false, doff, ring, &last_split);
+        decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, false, doff, ring);
       }
       pre.b = -1;
       ++r;

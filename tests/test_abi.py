@@ -52,17 +52,17 @@ def test_status_strings(lib):
 
 def test_default_partition_and_workspace_sizes(lib):
     assert lib.pa_default_partition_tokens() == 0  # automatic split size
-    # single split: no partials, only the per-sequence counters and the queue counter
-    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 2048) == 256 + 256
-    assert lib.pa_decode_workspace_bytes(512, 32, 64, 8, 0) == 2048 + 256  # automatic splits have >= 8 pages
+    # single split: no partials, only the (sequence, KV head) counters and the queue counter
+    assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 2048) == 64 * 8 * 4 + 256
+    assert lib.pa_decode_workspace_bytes(512, 32, 64, 8, 0) == 512 * 8 * 4 + 256  # automatic splits have >= 8 pages
     # automatic: partial rows for up to ceil(128 / 4) = 32 splits for up to 64 sequences, ceil(128 / 8) = 16 above
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 0) == lib.pa_decode_workspace_bytes(64, 32, 64, 128, 64)
     assert lib.pa_decode_workspace_bytes(65, 32, 64, 128, 0) == lib.pa_decode_workspace_bytes(65, 32, 64, 128, 128)
     assert lib.pa_decode_workspace_bytes(5000, 32, 64, 128, 0) == 0  # batch above the plan limit
-    # 8 splits of 256 tokens: part_o + part_m + part_l + one counter per sequence + the queue,
-    # each padded to 256 bytes
+    # 8 splits of 256 tokens: part_o + part_m + part_l + one counter per (sequence, KV head) + the
+    # queue, each padded to 256 bytes
     rows = 64 * 32 * 8
-    want = rows * 64 * 4 + 2 * (((rows * 4) + 255) // 256 * 256) + 256 + 256
+    want = rows * 64 * 4 + 2 * (((rows * 4) + 255) // 256 * 256) + 64 * 8 * 4 + 256
     assert lib.pa_decode_workspace_bytes(64, 32, 64, 128, 256) == want
     # partitions above 2048 tokens act as 2048
     assert lib.pa_decode_workspace_bytes(4, 32, 64, 256, 4096) == lib.pa_decode_workspace_bytes(4, 32, 64, 256, 2048) > 0

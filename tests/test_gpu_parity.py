@@ -400,14 +400,14 @@ def test_workspace_reuse_and_counters_reset():
     outs = [ops.pa_decode(d.inputs[0]["q"], d.k_pool, d.v_pool, d.bt[0], d.seq_lens, lay.scale,
                           partition_tokens=part, workspace=ws).clone() for _ in range(3)]
     torch.cuda.synchronize()
-    # workspace layout: part_o, part_m, part_l, int32 counters [B], int32 queue [2], each padded
+    # workspace layout: part_o, part_m, part_l, int32 counters [B][8], int32 queue [2], each padded
     # to 256 bytes; 16 sequences x 128 one-page splits exceed the grid, so the queue is in use
     rnd = lambda x: (x + 255) // 256 * 256
     rows = lay.B * 32 * (lay.max_blocks * 16 // part)
     off_c = rnd(rows * 64 * 4) + 2 * rnd(rows * 4)
-    off_q = off_c + rnd(lay.B * 4)
+    off_q = off_c + rnd(lay.B * 8 * 4)
     assert ws.numel() == off_q + 256
-    assert int(ws[off_c:off_c + lay.B * 4].view(torch.int32).abs().sum()) == 0
+    assert int(ws[off_c:off_c + lay.B * 8 * 4].view(torch.int32).abs().sum()) == 0
     assert int(ws[off_q:off_q + 8].view(torch.int32).abs().sum()) == 0
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
