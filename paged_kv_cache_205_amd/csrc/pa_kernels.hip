@@ -587,10 +587,19 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   for (int r = 0; r < 4; ++r) {
     const size_t row = ((size_t)b * kQHeads + g * kGroup + r) * a.S + s;
     __hip_atomic_store(a.part_o + row * kHeadDim + d, o[r] / lr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) {
-      __hip_atomic_store(a.part_m + row, mr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.part_l + row, lr[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  }
+  {
+    // m and l of the 4 heads in one store with every lane active: lane i
+    // writes m (i & 4 clear) or l of head i & 3, and lanes that agree on
+    // i & 7 write the same word with the same value.  (A store by lane 0
+    // alone puts the stores in a branch, and the compiler then waits for
+    // the first ones to complete before it issues the rest.)
+    const int r = lane & 3;
+    const float mv = r == 0 ? mr[0] : r == 1 ? mr[1] : r == 2 ? mr[2] : mr[3];
+    const float lv = r == 0 ? lr[0] : r == 1 ? lr[1] : r == 2 ? lr[2] : lr[3];
+    const size_t row = ((size_t)b * kQHeads + g * kGroup + r) * a.S + s;
+    __hip_atomic_store((lane & 4) ? a.part_l + row : a.part_m + row, (lane & 4) ? lv : mv, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
   wait_vmcnt<0>();
 
