@@ -340,7 +340,8 @@ struct ItemPrefetch {
 
 // One work item: split s (of nsplit) of sequence b, whose length is L, n of its
 // pages.  Called by all 8 waves of the workgroup with the same arguments; wave
-// g handles KV head g, and the waves do not wait for one another.
+// g handles KV head g, and the waves do not wait for one another.  A wave
+// returns with no load in flight (its output stores may be).
 template <bool kAppend, bool kRope>
 __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, int nsplit, int L, int n,
                                             const ItemPrefetch& pre, bool primed, DmaOffsets doff,
@@ -354,6 +355,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   const int c = lane >> 4;
 
   if (L <= 0) {  // empty sequence: zero its output rows
+    wait_vmcnt<0>();  // returns, like the other paths, with no load in flight
     reinterpret_cast<f32x4*>(a.out + ((size_t)b * kQHeads + g * kGroup) * kHeadDim)[lane] =
         f32x4{0.f, 0.f, 0.f, 0.f};
     return;
@@ -1074,13 +1076,15 @@ __global__ __launch_bounds__(512) void decode_kernel(DecodeArgs a) {
     const int act = __builtin_amdgcn_readfirstlane(plan_lds.active);
     if (!a.queue || __builtin_amdgcn_readfirstlane(sA[B]) + __builtin_amdgcn_readfirstlane(sC[B]) <= act) break;
     // Wave 0 claims the next item as soon as it is done; the first barrier also
-    // ensures every wave has read the previous next_item.
+    // ensures every wave has read the previous next_item.  The barriers wait on
+    // LDS only: the item's output stores need not complete before the claim
+    // (a __syncthreads would wait for them, a round trip before the claim).
     int fetched = 0;
     if (threadIdx.x == 0)
       fetched = act + __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
+    lds_barrier();
     if (threadIdx.x == 0) next_item = fetched;
-    __syncthreads();
+    lds_barrier();
     const int i = __builtin_amdgcn_readfirstlane(next_item);
     const int n_multi = __builtin_amdgcn_readfirstlane(sA[B]);
     const int n_items = n_multi + __builtin_amdgcn_readfirstlane(sC[B]);
@@ -1408,6 +1412,8 @@ __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
         int n = L > 0 ? (L + kPageTokens - 1) / kPageTokens : 0;
         n = (n - s + nsplit - 1) / nsplit;
         decode_item<kAppend, kRope>(a, b, s, nsplit, L, n, pre, false, doff, ring);
+      } else {
+        wait_vmcnt<0>();  // what decode_item guarantees on return: no load in flight
       }
       pre.b = -1;
       ++r;
@@ -1416,17 +1422,19 @@ __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
         continue;
       }
       if (!queued) break;
-      // claim one of the items after the fixed rounds; the first barrier also
-      // ensures every wave has read the previous next_item and that every
-      // wave's copies of the queued slots have landed (claiming while the item
-      // still streams was slower: the workgroups of a round claim together)
-      wait_vmcnt<0>();
+      // claim one of the items after the fixed rounds (claiming while the item
+      // still streams was slower: the workgroups of a round claim together).
+      // Every wave's copies of the queued slots have landed: decode_item
+      // returns with no load in flight, only its output stores, which the
+      // claim does not wait for; the first barrier also ensures every wave
+      // has read the previous next_item.  The barriers wait on LDS only (a
+      // __syncthreads would wait for the stores, a round trip before the claim).
       int fetched = 0;
       if (threadIdx.x == 0)
         fetched = n_fixed + __hip_atomic_fetch_add(a.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
+      lds_barrier();
       if (threadIdx.x == 0) next_item = fetched;
-      __syncthreads();
+      lds_barrier();
       const int i = __builtin_amdgcn_readfirstlane(next_item);
       if (i >= n_items) break;
       it = i - n_fixed < n_stage ? *reinterpret_cast<const int4*>(stage + (size_t)(i - n_fixed) * 16) : slots[i];
