@@ -282,8 +282,9 @@ int32_t pa_default_partition_tokens(void);
  *                of a sequence depend only on its own length, so its output is
  *                bit-identical whatever else is in the batch.  With 0
  *                (automatic) pp = clamp(ceil(total pages of the batch / n), m,
- *                128) with n = 192 when every sequence has the same page count
- *                and 384 otherwise, and m = 4 for B <= 64, 8 above (the
+ *                128) with n = 192 when every sequence has the same page count,
+ *                otherwise n = 240 when total pages >= 8 B and 384 below, and
+ *                m = 4 for B <= 64, 8 above (the
  *                smallest split): large batches get few, long splits and
  *                small or skewed batches get more; results then may differ in
  *                rounding between batches.  When S_b > 1 the splits' partial

@@ -664,12 +664,13 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 // Work plan.  Every workgroup builds the same plan in LDS from seq_lens:
 //   pp      pages per split: a.part_pages if set, else ceil(total pages / n)
 //           clamped to [m, 128], n = 192 when every sequence has the same page
-//           count and 384 for mixed lengths (about n items), m = 4 for batches
-//           of at most 64 sequences and 8 above;
+//           count, and for mixed lengths 240 when sequences average 8 pages
+//           or more, 384 below (about n items), m = 4 for batches of at most
+//           64 sequences and 8 above;
 //   nsplit  ceil(npages / pp) splits per sequence (1 for an empty sequence);
 //   items   first every split of the multi-split sequences (sequence-major),
 //           then the single-split sequences (longest first, by 16-page
-//           bucket, when the queue is in use and items are long on average).
+//           bucket, when the queue is in use and items average 8 pages or more).
 //           Workgroup w starts with item w; if there are more items than
 //           workgroups the rest are handed out by an atomic queue.  Long
 //           sequences' splits, the largest items, start first.
@@ -682,6 +683,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
 constexpr int kTargetItems = 192;          // batches with one page count (and the host's guess)
 constexpr int kLongItemPages = 8;          // items averaging this many pages run one workgroup per CU
 constexpr int kTargetItemsMixed = 384;     // batches of mixed lengths (the queue takes what the active workgroups do not)
+constexpr int kTargetItemsMixedLong = 240; // the same when sequences average kLongItemPages pages or more
 constexpr int kAutoMinPages = 8;
 constexpr int kMaxSplitPages = 128;
 // Length buckets for handing out single-split items longest first: bucket k
@@ -695,6 +697,16 @@ __host__ __device__ __forceinline__ int auto_min_pages(int B) { return B <= 64 ?
 __host__ __device__ __forceinline__ int auto_pages_per_split(int total_pages, int target = kTargetItems,
                                                              int minp = kAutoMinPages) {
   return min(kMaxSplitPages, max(minp, (total_pages + target - 1) / target));
+}
+// Items an automatic split aims at.  One page count: about 192, which suits
+// streaming whole pages with one item per workgroup.  Mixed lengths: more,
+// smaller items, so that long sequences are not left to a few workgroups at
+// the end; about 384 when sequences are short on average (their items run two
+// workgroups per CU), 240 when they average 8 pages or more (one workgroup per
+// CU; on the fragmented workload 23-24 pages per split measured 631-633 us per
+// step against 643-663 us at 15, 22 and 26-27 pages).
+__host__ __device__ __forceinline__ int auto_target_items(bool uniform, int total_pages, int B) {
+  return uniform ? kTargetItems : total_pages >= kLongItemPages * B ? kTargetItemsMixedLong : kTargetItemsMixed;
 }
 
 __device__ __forceinline__ int active_workgroups(int total_pages, int n_items, int narrow) {
@@ -818,12 +830,9 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
     all_max = max(all_max, pl->wave_max[v]);
     all_min_c = max(all_min_c, pl->wave_min[v]);
   }
-  // One page count for every sequence: about 192 items, which suits streaming
-  // whole pages with one item per workgroup.  Mixed lengths: about 384 smaller
-  // items, so that long sequences are not left to a few workgroups at the end.
   const bool uniform = kPageCap - all_min_c == all_max;
   const int pp = part_pages > 0 ? part_pages
-                                : auto_pages_per_split(total_pages, uniform ? kTargetItems : kTargetItemsMixed,
+                                : auto_pages_per_split(total_pages, auto_target_items(uniform, total_pages, B),
                                                        auto_min_pages(B));
   ItemPlan p;
   p.pp = pp;
@@ -869,10 +878,11 @@ __device__ __forceinline__ ItemPlan plan_finish(PlanLengths x, int B, int part_p
   }
   const int i0 = blockIdx.x;
   const int active = active_workgroups(total_pages, n_multi + n_single, narrow);
-  // When the queue hands out items and they are long on average, the
-  // single-split items go longest first (by 16-page length bucket, into sC), so
-  // that no long item starts late; otherwise they keep sequence order.
-  const bool by_length = n_multi + n_single > active && total_pages >= 16 * (n_multi + n_single);
+  // When the queue hands out items and they are long on average (the batches
+  // that run one workgroup per CU), the single-split items go longest first (by
+  // 16-page length bucket, into sC), so that no long item starts late;
+  // otherwise they keep sequence order.
+  const bool by_length = n_multi + n_single > active && total_pages >= kLongItemPages * (n_multi + n_single);
   for (int b = b0; b < b1; ++b) {
     const int ns = nsplit_of(sL[b], pp);
     sA[b] = oa;
@@ -1216,7 +1226,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   const int total = s_red[0], all_max = s_red[1];
   const bool uniform = kPageCap - s_red[2] == all_max;
   const int pp = part_pages > 0 ? part_pages
-                                : auto_pages_per_split(total, uniform ? kTargetItems : kTargetItemsMixed, auto_min_pages(B));
+                                : auto_pages_per_split(total, auto_target_items(uniform, total, B), auto_min_pages(B));
   PlanHeader h;
   h.magic = kPlanMagic;
   h.B = B;

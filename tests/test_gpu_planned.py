@@ -41,7 +41,7 @@ def expected_splits(lens, partition_tokens):
         pp = min(partition_tokens, 2048) // 16
     else:
         uniform = pages.min() == pages.max()
-        n = 192 if uniform else 384
+        n = 192 if uniform else (240 if int(pages.sum()) >= 8 * B else 384)
         m = 4 if B <= 64 else 8
         pp = min(128, max(m, -(-int(pages.sum()) // n)))
     return np.where(lens > 0, -(-pages // pp), 1), pp

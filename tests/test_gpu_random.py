@@ -105,8 +105,8 @@ def queued_case(seed, B=300, max_blocks=128):
 
 def test_queued_longest_first_batch_matches_oracle():
     """300 sequences of up to 2048 tokens: under the automatic split the plan
-    has more items (about 500) than the one-per-CU workgroups that take them,
-    averaging over 16 pages, so single-split items are handed out longest
+    has more items (about 420) than the one-per-CU workgroups that take them,
+    averaging over 8 pages, so single-split items are handed out longest
     first through the queue.  Every output is compared with the oracle."""
     q, kp, vp, bt, L = queued_case(4242)
     say(f"queued decode B={len(L)} tokens={int(L.sum())} (oracle ...)")
