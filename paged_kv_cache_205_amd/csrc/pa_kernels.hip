@@ -1345,11 +1345,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 }
 
 // Decode from a plan: the item code of decode_kernel, with the items read from
-// the plan's slots instead of a plan built in every workgroup.  The header, this
-// workgroup's first slot and the rows of the item it would get if every
-// sequence filled its table row (as in decode_kernel) load together; the next
-// fixed round's slot loads while an item runs; after the fixed rounds the
-// workgroup claims the remaining items through the queue counter.
+// the plan's slots instead of a plan built in every workgroup.  The header and
+// this workgroup's first slot load together (no rows are loaded on a guess of
+// the first item, as decode_kernel does: for mixed batches the guess misses,
+// and its loads delayed the first item's own); the next fixed round's slot
+// loads while an item runs; after the fixed rounds the workgroup claims the
+// remaining items through the queue counter.
 template <bool kAppend, bool kRope>
 __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1361,25 +1362,8 @@ __global__ __launch_bounds__(512) void decode_planned_kernel(DecodeArgs a) {
   const int4* slots = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(a.plan) + kPlanHeaderBytes);
   const int hv = a.plan[min(lane, (int)(sizeof(PlanHeader) / sizeof(int)) - 1)];  // lane i: header word i
   int4 it = slots[w];
-
-  const int ns_g = a.guess_ns;
-  const int b_raw = ns_g > 1 ? (int)__umulhi(blockIdx.x, a.guess_magic) : (int)blockIdx.x;
-  const int b_g = min(b_raw, a.B - 1);
-  ItemPrefetch pre;
-  pre.b = (a.max_blocks <= 128 && b_raw < a.B) ? b_raw : -1;
-  {
-    const int t = lane & 15, c = lane >> 4;
-    const int g = threadIdx.x >> 6;
-    const int32_t* bt = a.block_table + (size_t)b_g * a.max_blocks;
-    pre.id0 = bt[min(lane, a.max_blocks - 1)];
-    pre.id1 = bt[min(64 + lane, a.max_blocks - 1)];
-    const uint16_t* qrow = a.q + ((size_t)b_g * kQHeads + g * kGroup + (t & 3)) * kHeadDim;
-    pre.q0 = ld16(qrow + 8 * c);
-    pre.q1 = ld16(qrow + 32 + 8 * c);
-    pre.row = u32x4{0u, 0u, 0u, 0u};
-    if (kAppend)
-      pre.row = ld16(((lane & 8) ? a.v_new : a.k_new) + ((size_t)b_g * kKvHeads + g) * kHeadDim + 8 * (lane & 7));
-  }
+  ItemPrefetch pre = {};
+  pre.b = -1;  // nothing prefetched
   const DmaOffsets doff = dma_offsets(lane, threadIdx.x >> 6);
   const int magic = __builtin_amdgcn_readlane(hv, 0);
   const int pB = __builtin_amdgcn_readlane(hv, 1);
