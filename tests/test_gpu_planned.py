@@ -178,6 +178,36 @@ def test_planned_random_batches(seed):
         check_close(got[L > 0], ref[L > 0], f"seed {seed} partition {part}")
 
 
+@pytest.mark.parametrize("extra_page", [0, 1])
+def test_split_target_boundary(extra_page):
+    """The automatic split aims at about 240 items once a mixed batch holds
+    8 pages per sequence on average, 384 below: 300 sequences of 4 and 12 pages
+    hold exactly 2400 pages (10 pages per split) and, with one page fewer, 2399
+    (the 8-page minimum).  Plans, bit-identity with the unplanned call and the
+    oracle on every sequence, on both sides of the bound."""
+    B, max_blocks = 300, 128
+    lens = np.array([64 if b % 2 == 0 else 192 for b in range(B)], np.int64)
+    if not extra_page:
+        lens[1] = 176  # 11 pages instead of 12
+    total = int(((lens + 15) // 16).sum())
+    assert total == (2400 if extra_page else 2399)
+    q, kp, vp, bt, L = random_case(7 + extra_page, Hq=32, Hkv=8, D=64, max_blocks=max_blocks,
+                                   lens=[int(x) for x in lens])
+    ref = decode_ref(q, kp, vp, bt, L, 0.125)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    qd, kd, vd = dev(q), dev(kp), dev(vp)
+    btd, sl = torch.from_numpy(bt).cuda(), torch.from_numpy(L).cuda()
+    say(f"split target boundary: {total} pages over {B} sequences")
+    plan = ops.pa_decode_plan(sl, max_blocks, 0)
+    torch.cuda.synchronize()
+    hdr = check_plan(plan, L, max_blocks, 0)
+    assert hdr["pp"] == (10 if extra_page else 8)
+    a = ops.pa_decode(qd, kd, vd, btd, sl, 0.125)
+    p = ops.pa_decode_planned(qd, kd, vd, btd, plan, 0.125)
+    assert torch.equal(a, p)
+    check_close(p.cpu().numpy(), ref, f"{total} pages")
+
+
 @pytest.mark.parametrize("name", ["fragmented", "skewed", "large", "full"])
 def test_planned_full_size(name):
     """Every layer of the full-size workloads: planned append + decode bit-identical
