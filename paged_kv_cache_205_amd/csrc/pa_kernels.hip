@@ -196,14 +196,31 @@ __device__ __forceinline__ DmaOffsets dma_offsets(int lane, int g) {
                     (uint32_t)(tau1 * kRowElems + g * kHeadDim + 8 * ((lane & 7) ^ swz(tau1)))};
 }
 // Starts the copy of head g's K and V tiles of one page into an LDS slot.
-__device__ __forceinline__ void issue_page(const DecodeArgs& a, unsigned char* dst, int32_t page, DmaOffsets o) {
+// Only token rows below `rows` are read (the last page of a sequence holds
+// fewer tokens); the rows past them keep what the slot held, and attend_page
+// masks them.  Every copy instruction is issued with at least one row (the
+// second one keeps row 8), so each page counts as 4 loads in the waits.
+__device__ __forceinline__ void issue_page(const DecodeArgs& a, unsigned char* dst, int32_t page, DmaOffsets o,
+                                           int rows = kPageTokens) {
   const size_t base = (size_t)(uint32_t)page * (size_t)(kPageTokens * kRowElems);
   const uint16_t* kp = a.k_pool + base;
   const uint16_t* vp = a.v_pool + base;
-  __builtin_amdgcn_global_load_lds(kp + o.off0, dst, 16, 0, 2);
-  __builtin_amdgcn_global_load_lds(kp + o.off1, dst + 1024, 16, 0, 2);
-  __builtin_amdgcn_global_load_lds(vp + o.off0, dst + kTileBytes, 16, 0, 2);
-  __builtin_amdgcn_global_load_lds(vp + o.off1, dst + kTileBytes + 1024, 16, 0, 2);
+  if (rows >= kPageTokens) {  // a full page (wave-uniform): no lane masks
+    __builtin_amdgcn_global_load_lds(kp + o.off0, dst, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(kp + o.off1, dst + 1024, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(vp + o.off0, dst + kTileBytes, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(vp + o.off1, dst + kTileBytes + 1024, 16, 0, 2);
+    return;
+  }
+  const int row = (threadIdx.x & 63) >> 3;  // rows row and 8 + row of the two halves
+  if (row < rows) {
+    __builtin_amdgcn_global_load_lds(kp + o.off0, dst, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(vp + o.off0, dst + kTileBytes, 16, 0, 2);
+  }
+  if (row == 0 || 8 + row < rows) {
+    __builtin_amdgcn_global_load_lds(kp + o.off1, dst + 1024, 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(vp + o.off1, dst + kTileBytes + 1024, 16, 0, 2);
+  }
 }
 
 // One page of a split: S^T = K Q^T on MFMA, the online-softmax update of the
@@ -443,7 +460,10 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
     qs1 = *reinterpret_cast<const f32x4*>(cs + 36);
   }
 
-  auto issue = [&](int slot, int32_t page) { issue_page(a, ring[g][slot], page, doff); };
+  // the k-th page of the split is page s + k nsplit of the sequence
+  auto issue = [&](int slot, int k, int32_t page) {
+    issue_page(a, ring[g][slot], page, doff, min(kPageTokens, L - (s + k * nsplit) * kPageTokens));
+  };
   // LDS read offsets: K (A operand) token t, chunks c and 4+c; V^T element
   // (token 4c+q, dim 16nn+t) lives in chunk 2nn + t/8 at element t%8.
   const int kr0 = t * 128 + 16 * (c ^ swz(t));
@@ -471,7 +491,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
   if (!primed) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u)
-      if (u < n) issue(u, page_of(u));
+      if (u < n) issue(u, u, page_of(u));
   }
 
   if (kRope) {
@@ -545,7 +565,7 @@ __device__ __forceinline__ void decode_item(const DecodeArgs& a, int b, int s, i
         for (int q = 0; q < 4; ++q) vb[nn][q] = *reinterpret_cast<const short*>(tile + vr[nn][q]);
       wait_lgkmcnt0();  // slot fully read: refill it
       __builtin_amdgcn_sched_barrier(0);
-      if (k + kRing < n) issue(u, page_of(k + kRing));
+      if (k + kRing < n) issue(u, k + kRing, page_of(k + kRing));
 
       attend_page(k0, k1, vb, qb0, qb1, s + k * nsplit, L, c, a.scale_log2, m_lane, l_lane, acc);
     }
