@@ -85,10 +85,13 @@ __device__ __forceinline__ int prompt_start(const int32_t* cu, int B, int r) {
 }
 
 // Running state of one wave: O^T accumulators, per-(query, head) maximum and
-// per-lane partial row sums.
+// per-lane partial row sums.  The exponent offset and the raise threshold are
+// kept beside the maximum, so a tile that does not raise it recomputes neither.
 struct WaveState {
   f32x4 acc[4][4];  // [head][d tile]: O^T rows 16dt + 4c .. +3, query t
   float m[4];       // running maximum (base 2), the same in the 4 lanes of a query
+  float nm[4];      // -m, or 0 while m is -inf: the exponent offset
+  float thr[4];     // m + kSlack: a larger scaled score raises the maximum
   float l[4];       // bf16-pair weights: this lane's share of the row sum
   f32x4 lsum[4];    // fp16 weights: the row sum of the rounded weights (every register)
 };
@@ -189,7 +192,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, float (&sv)[4][8], floa
 #pragma unroll
     for (int i = 0; i < 8; ++i) x = fmaxf(x, sv[h][i]);
     xm[h] = x * c2;
-    raise |= xm[h] > ws.m[h] + kSlack;
+    raise |= xm[h] > ws.thr[h];
   }
   // Lazy maximum: the running maximum moves only when a score exceeds it by
   // more than kSlack (base 2), so weights stay below 2^kSlack in between.
@@ -201,6 +204,8 @@ __device__ __forceinline__ void tile_step(WaveState& ws, float (&sv)[4][8], floa
       const float mn = fmaxf(ws.m[h], tm);
       const float alpha = (mn == ws.m[h]) ? 1.f : __builtin_amdgcn_exp2f(ws.m[h] - mn);
       ws.m[h] = mn;
+      ws.nm[h] = mn == -INFINITY ? 0.f : -mn;
+      ws.thr[h] = mn + kSlack;
       if (kF16)
         ws.lsum[h] *= alpha;
       else
@@ -236,7 +241,7 @@ __device__ __forceinline__ void tile_step(WaveState& ws, float (&sv)[4][8], floa
 
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const float nm = ws.m[h] == -INFINITY ? 0.f : -ws.m[h];
+    const float nm = ws.nm[h];
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[h][i], c2, nm));
@@ -370,6 +375,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) ws.acc[h][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     ws.m[h] = -INFINITY;
+    ws.nm[h] = 0.f;
+    ws.thr[h] = -INFINITY;
     ws.l[h] = 0.f;
     ws.lsum[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
