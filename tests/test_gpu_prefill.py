@@ -1,7 +1,8 @@
 """pa_prefill (causal GQA attention of whole prompts over their own K and V) on
 the GPU against the FP64 oracle: ragged prompt batches spanning several 64-row
 blocks with ragged tails, prompt boundaries inside and at the edges of 16-row
-groups, empty and one-token prompts, scale extremes, the largest batch, and
+groups, empty and one-token prompts, scale extremes, scores that raise the
+running maximum in every tile, the largest batch, and
 the full 64 x 2047-row prompt workload (one whole prompt plus sampled rows of
 every other).  Tolerance: 2e-3 absolute, 1e-2 row-relative (tests/helpers)."""
 import numpy as np
@@ -115,6 +116,29 @@ def test_scales(scale, sigma_k, weights):
         check_fp16_weights(got, ref, v_spread(v, cu), f"scale {scale} sigma_k {sigma_k}")
     else:
         check_close(got, ref, f"scale {scale} sigma_k {sigma_k}")
+
+
+@pytest.mark.parametrize("weights", ["bf16x2", "fp16"])
+def test_running_maximum_raised_every_tile(weights):
+    """Scores that grow along each prompt by about 11 (base 2) per 32-key tile,
+    more than the lazy maximum's slack of 8: every tile raises the running
+    maximum and rescales what the rows have accumulated."""
+    lens = [300, 97, 1, 64]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.float32)
+
+    def bits(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    q = bits(np.full((T, 32, 64), 0.125))  # q . k = 0.24 pos, 0.35 pos in base-2 logits at scale 1
+    k = bits(np.broadcast_to((0.03 * pos)[:, None, None], (T, 8, 64)))
+    v = rand_bits(np.random.default_rng(15), (T, 8, 64))
+    got, ref = run(q, k, v, cu, 1.0, weights), prefill_ref(q, k, v, cu, 1.0)
+    if weights == "fp16":
+        check_fp16_weights(got, ref, v_spread(v, cu), "raised every tile")
+    else:
+        check_close(got, ref, "raised every tile")
 
 
 def test_scale_zero_gives_running_means():
