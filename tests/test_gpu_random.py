@@ -10,9 +10,11 @@ are kept so that the oracle finishes in seconds: entries that are not full
 rows are scaled down to about 12k attended tokens per case, full rows (L = 16
 x table width) are kept as they are.
 
-The last test is a batch with more and longer items than the workgroups that
-take them, so that the automatic plan hands single-split items out longest
-first through the queue, compared in full.
+Another is a batch with more and longer items than the workgroups that take
+them, so that the automatic plan hands single-split items out longest first
+through the queue, compared in full.  The last puts scores that rise (or fall)
+steadily along each sequence, so that every page raises the running maximum
+(or only a split's first page sets it).
 """
 import numpy as np
 import pytest
@@ -119,3 +121,26 @@ def test_queued_longest_first_batch_matches_oracle():
         empty = L == 0
         assert np.all(got[empty] == 0.0), "empty sequences give zeros"
         check_close(got[~empty], ref[~empty], f"queued batch partition {part}")
+
+
+@pytest.mark.parametrize("rising", [True, False])
+def test_scores_that_rise_or_fall_along_the_sequence(rising):
+    """Keys that make the scores rise by about 5.5 (base 2) per page, so that
+    every page raises the running maximum and rescales what the split holds, or
+    fall the same way, so that only a split's first page sets it.  Several
+    splits per sequence and one page per split included."""
+    lens = [2048, 700, 33, 16, 1]
+    q, kp, vp, bt, L = random_case(77, Hq=32, Hkv=8, D=64, max_blocks=128, lens=lens)
+    for b, n in enumerate(L):
+        t = np.arange(int(n))
+        ramp = 0.03 * (t if rising else (int(n) - 1 - t))
+        vals = torch.from_numpy(np.repeat(ramp.astype(np.float32), 8 * 64).reshape(int(n), 8, 64))
+        kp[bt[b, t // 16], t % 16] = vals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    q[:] = 0x3E00  # 0.125: q . k = 0.24 t, 0.35 t in base-2 logits at scale 1
+    ref = decode_ref(q, kp, vp, bt, L, 1.0)
+    qd, kd, vd = dev_bf16(q), dev_bf16(kp), dev_bf16(vp)
+    btd, sl = torch.from_numpy(bt).cuda(), torch.from_numpy(L).cuda()
+    for part in (0, 16, 256):
+        say(f"{'rising' if rising else 'falling'} scores, partition={part}")
+        got = ops.pa_decode(qd, kd, vd, btd, sl, 1.0, partition_tokens=part).cpu().numpy()
+        check_close(got, ref, f"{'rising' if rising else 'falling'} scores, partition {part}")
