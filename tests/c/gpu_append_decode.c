@@ -1,11 +1,14 @@
 /* A plain C11 caller of the library on the GPU.  It builds a small paged state
  * with a fixed generator, places it in device memory from hipMalloc, calls
  * pa_append_decode through include/pa.h on the default stream (the automatic
- * split, then one page per split), and writes its inputs and results to the
- * file named by its argument, for the Python test to check against the oracle:
+ * split, then one page per split), then the same two steps planned
+ * (pa_decode_plan, pa_decode_planned), and writes its inputs and results to
+ * the file named by its argument, for the Python test to check against the
+ * oracle:
  *   q [B][32][64], k_new, v_new [B][8][64], block_table [B][4], seq_lens [B],
  *   K and V pools before [12][16][8][64] (bf16 bits), K and V pools after,
- *   out [2][B][32][64] (fp32).
+ *   out [4][B][32][64] (fp32: unplanned automatic, unplanned one page,
+ *   planned automatic, planned one page).
  * Exit status: 0, or the step that failed (its status printed on stderr). */
 #include <stdint.h>
 #include <stdio.h>
@@ -46,7 +49,7 @@ int main(int argc, char** argv) {
   }
   static uint16_t q[Q_ELEMS], k_new[NEW_ELEMS], v_new[NEW_ELEMS], kp[POOL_ELEMS], vp[POOL_ELEMS];
   static uint16_t kp_after[POOL_ELEMS], vp_after[POOL_ELEMS];
-  static float out[2][Q_ELEMS];
+  static float out[4][Q_ELEMS];
   /* three sequences after the append: 37 tokens on pages 7, 2, 10; 16 on page 4; 1 on page 11 */
   const int32_t bt[B][MAXB] = {{7, 2, 10, -1}, {4, -1, -1, -1}, {11, -1, -1, -1}};
   const int32_t lens[B] = {37, 16, 1};
@@ -56,14 +59,17 @@ int main(int argc, char** argv) {
   for (size_t i = 0; i < POOL_ELEMS; ++i) kp[i] = next_bf16();
   for (size_t i = 0; i < POOL_ELEMS; ++i) vp[i] = next_bf16();
 
-  void *dq, *dk_new, *dv_new, *dkp, *dvp, *dbt, *dlens, *dout, *dws;
+  void *dq, *dk_new, *dv_new, *dkp, *dvp, *dbt, *dlens, *dout, *dws, *dplan;
   const size_t ws_bytes = pa_decode_workspace_bytes(B, HQ, D, MAXB, PT);  /* the larger of the two splits */
-  if (ws_bytes == 0) return 3;
+  const size_t plan_bytes = pa_decode_plan_bytes(B, MAXB, PT) > pa_decode_plan_bytes(B, MAXB, 0)
+                                ? pa_decode_plan_bytes(B, MAXB, PT)
+                                : pa_decode_plan_bytes(B, MAXB, 0);
+  if (ws_bytes == 0 || plan_bytes == 0) return 3;
   if (check(hipMalloc(&dq, sizeof q), "hipMalloc") || check(hipMalloc(&dk_new, sizeof k_new), "hipMalloc") ||
       check(hipMalloc(&dv_new, sizeof v_new), "hipMalloc") || check(hipMalloc(&dkp, sizeof kp), "hipMalloc") ||
       check(hipMalloc(&dvp, sizeof vp), "hipMalloc") || check(hipMalloc(&dbt, sizeof bt), "hipMalloc") ||
       check(hipMalloc(&dlens, sizeof lens), "hipMalloc") || check(hipMalloc(&dout, sizeof out[0]), "hipMalloc") ||
-      check(hipMalloc(&dws, ws_bytes), "hipMalloc"))
+      check(hipMalloc(&dws, ws_bytes), "hipMalloc") || check(hipMalloc(&dplan, plan_bytes), "hipMalloc"))
     return 4;
   if (check(hipMemcpy(dq, q, sizeof q, hipMemcpyHostToDevice), "copy") ||
       check(hipMemcpy(dk_new, k_new, sizeof k_new, hipMemcpyHostToDevice), "copy") ||
@@ -89,6 +95,21 @@ int main(int argc, char** argv) {
         check(hipMemcpy(out[c], dout, sizeof out[c], hipMemcpyDeviceToHost), "copy back"))
       return 7;
   }
+  for (int c = 0; c < 2; ++c) {
+    /* the same steps with the plan built once, as for the layers of a step */
+    int st = pa_decode_plan((const int32_t*)dlens, B, MAXB, partitions[c], dplan, plan_bytes, NULL);
+    if (st == PA_OK)
+      st = pa_decode_planned((const uint16_t*)dq, (const uint16_t*)dk_new, (const uint16_t*)dv_new, NULL, 0,
+                             (uint16_t*)dkp, (uint16_t*)dvp, (const int32_t*)dbt, MAXB, 0.125f, (float*)dout, B, HQ,
+                             HKV, D, PAGES, partitions[c], dplan, plan_bytes, dws, ws_bytes, NULL);
+    if (st != PA_OK) {
+      fprintf(stderr, "planned decode (partition %d): %s\n", partitions[c], pa_status_string(st));
+      return 6;
+    }
+    if (check(hipDeviceSynchronize(), "synchronize") ||
+        check(hipMemcpy(out[2 + c], dout, sizeof out[2 + c], hipMemcpyDeviceToHost), "copy back"))
+      return 7;
+  }
   if (check(hipMemcpy(kp_after, dkp, sizeof kp_after, hipMemcpyDeviceToHost), "copy back") ||
       check(hipMemcpy(vp_after, dvp, sizeof vp_after, hipMemcpyDeviceToHost), "copy back"))
     return 7;
@@ -102,6 +123,6 @@ int main(int argc, char** argv) {
            fwrite(vp_after, sizeof vp_after, 1, f) == 1 && fwrite(out, sizeof out, 1, f) == 1;
   ok = (fclose(f) == 0) && ok;
   hipFree(dq), hipFree(dk_new), hipFree(dv_new), hipFree(dkp), hipFree(dvp);
-  hipFree(dbt), hipFree(dlens), hipFree(dout), hipFree(dws);
+  hipFree(dbt), hipFree(dlens), hipFree(dout), hipFree(dws), hipFree(dplan);
   return ok ? 0 : 9;
 }

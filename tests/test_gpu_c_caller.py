@@ -1,8 +1,10 @@
 """The library driven from plain C on the GPU: tests/c/gpu_append_decode.c
 (C11, gcc, include/pa.h, hipMalloc'd buffers, the default stream) calls
-pa_append_decode under the automatic split and under one page per split, and
-dumps its inputs and results.  The pools must equal the oracle's append bit
-for bit, and both outputs must match the FP64 decode of the appended pools."""
+pa_append_decode under the automatic split and under one page per split, then
+the same through a plan (pa_decode_plan, pa_decode_planned), and dumps its
+inputs and results.  The pools must equal the oracle's append bit for bit,
+every output must match the FP64 decode of the appended pools, and each planned
+output must equal the unplanned one of the same split bit for bit."""
 import os
 import shutil
 import subprocess
@@ -36,7 +38,7 @@ def read_dump(path):
              bt=take(np.int32, (B, MAXB)), lens=take(np.int32, (B,)),
              kp=take(np.uint16, (PAGES, PT, HKV, D)), vp=take(np.uint16, (PAGES, PT, HKV, D)),
              kp_after=take(np.uint16, (PAGES, PT, HKV, D)), vp_after=take(np.uint16, (PAGES, PT, HKV, D)),
-             out=take(np.float32, (2, B, HQ, D)))
+             out=take(np.float32, (4, B, HQ, D)))
     assert pos == len(raw), f"dump holds {len(raw)} bytes, expected {pos}"
     return d
 
@@ -57,7 +59,7 @@ def test_c_program_drives_append_decode(tmp_path):
            f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib", "-o", exe]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
-    say("C caller: pa_append_decode, automatic split and one page per split")
+    say("C caller: pa_append_decode and the planned decode, automatic split and one page per split")
     run = subprocess.run([exe, dump], capture_output=True, text=True, timeout=120)
     assert run.returncode == 0, f"exit {run.returncode}: {run.stderr}"
     d = read_dump(dump)
@@ -65,5 +67,8 @@ def test_c_program_drives_append_decode(tmp_path):
     assert np.array_equal(d["kp_after"], k_ref), "K pool after the C calls differs from the oracle's append"
     assert np.array_equal(d["vp_after"], v_ref), "V pool after the C calls differs from the oracle's append"
     ref = decode_ref(d["q"], k_ref, v_ref, d["bt"], d["lens"], 0.125)
-    for c, part in enumerate(("automatic", "one page")):
+    for c, part in enumerate(("automatic", "one page", "planned automatic", "planned one page")):
         check_close(d["out"][c], ref, f"C caller, {part} split")
+    for c in (0, 1):
+        assert np.array_equal(d["out"][2 + c].view(np.uint32), d["out"][c].view(np.uint32)), \
+            f"planned output {c} differs from the unplanned one"
