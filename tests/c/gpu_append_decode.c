@@ -2,13 +2,15 @@
  * with a fixed generator, places it in device memory from hipMalloc, calls
  * pa_append_decode through include/pa.h on the default stream (the automatic
  * split, then one page per split), then the same two steps planned
- * (pa_decode_plan, pa_decode_planned), and writes its inputs and results to
- * the file named by its argument, for the Python test to check against the
+ * (pa_decode_plan, pa_decode_planned) and through the allocation-free entry
+ * point (pa_append_decode_noalloc), and writes its inputs and results to the
+ * file named by its argument, for the Python test to check against the
  * oracle:
  *   q [B][32][64], k_new, v_new [B][8][64], block_table [B][4], seq_lens [B],
  *   K and V pools before [12][16][8][64] (bf16 bits), K and V pools after,
- *   out [4][B][32][64] (fp32: unplanned automatic, unplanned one page,
- *   planned automatic, planned one page).
+ *   out [6][B][32][64] (fp32: unplanned automatic, unplanned one page,
+ *   planned automatic, planned one page, allocation-free automatic,
+ *   allocation-free one page).
  * Exit status: 0, or the step that failed (its status printed on stderr). */
 #include <stdint.h>
 #include <stdio.h>
@@ -49,7 +51,7 @@ int main(int argc, char** argv) {
   }
   static uint16_t q[Q_ELEMS], k_new[NEW_ELEMS], v_new[NEW_ELEMS], kp[POOL_ELEMS], vp[POOL_ELEMS];
   static uint16_t kp_after[POOL_ELEMS], vp_after[POOL_ELEMS];
-  static float out[4][Q_ELEMS];
+  static float out[6][Q_ELEMS];
   /* three sequences after the append: 37 tokens on pages 7, 2, 10; 16 on page 4; 1 on page 11 */
   const int32_t bt[B][MAXB] = {{7, 2, 10, -1}, {4, -1, -1, -1}, {11, -1, -1, -1}};
   const int32_t lens[B] = {37, 16, 1};
@@ -108,6 +110,20 @@ int main(int argc, char** argv) {
     }
     if (check(hipDeviceSynchronize(), "synchronize") ||
         check(hipMemcpy(out[2 + c], dout, sizeof out[2 + c], hipMemcpyDeviceToHost), "copy back"))
+      return 7;
+  }
+  for (int c = 0; c < 2; ++c) {
+    /* the same steps with no workspace: the library's own scratch array */
+    const int st = pa_append_decode_noalloc((const uint16_t*)dk_new, (const uint16_t*)dv_new, (uint16_t*)dkp,
+                                            (uint16_t*)dvp, (const uint16_t*)dq, (const int32_t*)dbt, MAXB,
+                                            (const int32_t*)dlens, 0.125f, (float*)dout, B, HQ, HKV, D, PAGES,
+                                            partitions[c], NULL);
+    if (st != PA_OK) {
+      fprintf(stderr, "pa_append_decode_noalloc (partition %d): %s\n", partitions[c], pa_status_string(st));
+      return 6;
+    }
+    if (check(hipDeviceSynchronize(), "synchronize") ||
+        check(hipMemcpy(out[4 + c], dout, sizeof out[4 + c], hipMemcpyDeviceToHost), "copy back"))
       return 7;
   }
   if (check(hipMemcpy(kp_after, dkp, sizeof kp_after, hipMemcpyDeviceToHost), "copy back") ||

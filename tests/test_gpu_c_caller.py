@@ -1,10 +1,11 @@
 """The library driven from plain C on the GPU (C11, gcc, include/pa.h,
 hipMalloc'd buffers, the default stream).  tests/c/gpu_append_decode.c calls
 pa_append_decode under the automatic split and under one page per split, then
-the same through a plan (pa_decode_plan, pa_decode_planned): the pools must
-equal the oracle's append bit for bit, every output must match the FP64 decode
-of the appended pools, and each planned output must equal the unplanned one of
-the same split bit for bit.  tests/c/gpu_prefill.c fills three packed prompts
+the same through a plan (pa_decode_plan, pa_decode_planned) and through the
+allocation-free entry point (pa_append_decode_noalloc): the pools must equal
+the oracle's append bit for bit, every output must match the FP64 decode of the
+appended pools, and each planned or allocation-free output must equal the
+unplanned one of the same split bit for bit.  tests/c/gpu_prefill.c fills three packed prompts
 into their pages with pa_fill and runs pa_prefill in both weight modes: the
 pools must equal the oracle's fill bit for bit and the outputs must match the
 FP64 prefill (fp16 weights to their bound)."""
@@ -42,7 +43,7 @@ def read_dump(path):
              bt=take(np.int32, (B, MAXB)), lens=take(np.int32, (B,)),
              kp=take(np.uint16, (PAGES, PT, HKV, D)), vp=take(np.uint16, (PAGES, PT, HKV, D)),
              kp_after=take(np.uint16, (PAGES, PT, HKV, D)), vp_after=take(np.uint16, (PAGES, PT, HKV, D)),
-             out=take(np.float32, (4, B, HQ, D)))
+             out=take(np.float32, (6, B, HQ, D)))
     assert pos == len(raw), f"dump holds {len(raw)} bytes, expected {pos}"
     return d
 
@@ -70,18 +71,20 @@ def build_and_run(tmp_path, name):
 
 
 def test_c_program_drives_append_decode(tmp_path):
-    say("C caller: pa_append_decode and the planned decode, automatic split and one page per split")
+    say("C caller: pa_append_decode, the planned decode and the allocation-free call, two split sizes")
     dump = build_and_run(tmp_path, "gpu_append_decode")
     d = read_dump(dump)
     k_ref, v_ref = append_ref(d["kp"], d["vp"], d["k_new"], d["v_new"], d["bt"], d["lens"])
     assert np.array_equal(d["kp_after"], k_ref), "K pool after the C calls differs from the oracle's append"
     assert np.array_equal(d["vp_after"], v_ref), "V pool after the C calls differs from the oracle's append"
     ref = decode_ref(d["q"], k_ref, v_ref, d["bt"], d["lens"], 0.125)
-    for c, part in enumerate(("automatic", "one page", "planned automatic", "planned one page")):
+    names = ("automatic", "one page", "planned automatic", "planned one page", "allocation-free automatic",
+             "allocation-free one page")
+    for c, part in enumerate(names):
         check_close(d["out"][c], ref, f"C caller, {part} split")
-    for c in (0, 1):
-        assert np.array_equal(d["out"][2 + c].view(np.uint32), d["out"][c].view(np.uint32)), \
-            f"planned output {c} differs from the unplanned one"
+    for c in range(2, 6):
+        assert np.array_equal(d["out"][c].view(np.uint32), d["out"][c % 2].view(np.uint32)), \
+            f"{names[c]} output differs from the unplanned one"
 
 
 def test_c_program_drives_fill_and_prefill(tmp_path):
